@@ -58,7 +58,7 @@ def lib():
         L.oracle_expert_rows.restype = _i
         L.oracle_expert_rows.argtypes = [_i, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _i, _p]
         L.oracle_combine.restype = None
-        L.oracle_combine.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
+        L.oracle_combine.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p]
         L.oracle_forward.restype = _i64
         L.oracle_forward.argtypes = [_i] * 12 + [_p] * 10 + [_p] * 7
         _lib = L
@@ -165,8 +165,7 @@ def expert_rows(x_rows: np.ndarray, w13: np.ndarray, w2: np.ndarray, act: int,
 
 
 def combine(route_dst: np.ndarray, w: np.ndarray, y: np.ndarray,
-            y_shared: Optional[np.ndarray] = None,
-            token_bad: Optional[np.ndarray] = None) -> np.ndarray:
+            y_shared: Optional[np.ndarray] = None) -> np.ndarray:
     route_dst = np.ascontiguousarray(route_dst, dtype=np.int32)
     w = np.ascontiguousarray(w, dtype=np.float64)
     y = np.ascontiguousarray(y, dtype=np.float64)
@@ -175,9 +174,8 @@ def combine(route_dst: np.ndarray, w: np.ndarray, y: np.ndarray,
     if y.size == 0:
         y = np.zeros((1, max(H, 1)), np.float64)
     ysh = None if y_shared is None else np.ascontiguousarray(y_shared, dtype=np.float64)
-    tb = None if token_bad is None else np.ascontiguousarray(token_bad, dtype=np.uint8)
     out = np.zeros((T, H), np.float64)
-    lib().oracle_combine(T, k, H, _ptr(route_dst), _ptr(w), _ptr(y), _ptr(ysh), _ptr(tb), _ptr(out))
+    lib().oracle_combine(T, k, H, _ptr(route_dst), _ptr(w), _ptr(y), _ptr(ysh), _ptr(out))
     return out
 
 

@@ -140,9 +140,10 @@ int oracle_route(int T, int E, int k, int renormalize, const float *logits,
 /* Routes are numbered q = t*k + j.  A route is malformed when its expert id
  * is outside [0, E) or repeats an id of an earlier slot of the same token
  * (the negative / wide / duplicate route classes of the count-first
- * validation record).  A malformed route is neither counted nor placed; its
- * token is marked bad (its output row becomes NaN: MoEPacked's isolation of
- * malformed routes, PR 33963 commit text).
+ * validation record).  A malformed route is neither counted nor placed
+ * (route_dst = -2, distinct from a capacity drop) and its token is marked
+ * bad: its output row becomes NaN (MoEPacked's isolation of malformed
+ * routes, PR 33963 commit text).
  *
  * Count first: counts[e] = number of well-formed routes to expert e (raw,
  * before capacity).  Then prefix sums of the kept counts:
@@ -177,7 +178,7 @@ int64_t oracle_dispatch(int T, int E, int k, int C, const int32_t *ids,
         offsets[e + 1] = offsets[e] + (counts[e] < C ? counts[e] : C);
     if ((int64_t)offsets[E] > r_max) { free(ok); free(seen); return -1; }
     for (int64_t q = 0; q < nq; ++q) {
-        if (!ok[q]) { route_dst[q] = -1; continue; }
+        if (!ok[q]) { route_dst[q] = -2; continue; }
         int32_t e = ids[q];
         int64_t r = seen[e]++;
         if (r < C) {
@@ -259,11 +260,15 @@ int oracle_expert_rows(int n, int H, int I, int act, int x_fmt, const void *x,
 /* out[t] = sum over slots j (ascending) of w[t,j] * y[route_dst[t,j]],
  * skipping dropped routes (route_dst = -1, contributing zero; the kept
  * weights are not renormalised), plus y_shared[t] when given (shared experts
- * enter with weight 1).  A bad token's row is NaN. */
+ * enter with weight 1).  A token holding a malformed route (route_dst = -2)
+ * gets a NaN row. */
 void oracle_combine(int T, int k, int H, const int32_t *route_dst,
                     const double *w, const double *y, const double *y_shared,
-                    const uint8_t *token_bad, double *out) {
+                    double *out) {
     for (int t = 0; t < T; ++t) {
+        int bad = 0;
+        for (int j = 0; j < k; ++j)
+            if (route_dst[(int64_t)t * k + j] == -2) bad = 1;
         for (int o = 0; o < H; ++o) {
             double acc = 0.0;
             for (int j = 0; j < k; ++j) {
@@ -271,7 +276,7 @@ void oracle_combine(int T, int k, int H, const int32_t *route_dst,
                 if (row >= 0) acc += w[(int64_t)t * k + j] * y[(int64_t)row * H + o];
             }
             if (y_shared) acc += y_shared[(int64_t)t * H + o];
-            out[(int64_t)t * H + o] = (token_bad && token_bad[t]) ? NAN : acc;
+            out[(int64_t)t * H + o] = bad ? NAN : acc;
         }
     }
 }
@@ -345,7 +350,7 @@ int64_t oracle_forward(int T, int H, int E, int k, int I, int C, int act,
             for (int64_t i = 0; i < (int64_t)T * H; ++i) ysh[i] += ytmp[i];
         }
     }
-    oracle_combine(T, k, H, route_dst, w, y, ysh, bad, out);
+    oracle_combine(T, k, H, route_dst, w, y, ysh, out);
     free(bad); free(xd); free(y); free(ysh); free(ytmp);
     return n_bad;
 }

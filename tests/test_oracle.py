@@ -212,7 +212,11 @@ def test_malformed_routes_are_isolated(kind):
     valid = np.ones_like(ids, bool)
     valid[1] = [(0 <= e < E) and e not in ids[1, :j] for j, e in enumerate(ids[1])]
     assert d["counts"].sum() == valid.sum() == T * k - 1
-    assert np.all(d["route_dst"][~valid] == -1)
+    assert np.all(d["route_dst"][~valid] == -2)
+    # the combine poisons exactly the token holding the malformed route
+    y = np.ones((max(int(d["offsets"][-1]), 1), 3))
+    out = oracle.combine(d["route_dst"], np.full((T, k), 0.5), y)
+    assert np.all(np.isnan(out[1])) and np.all(np.isfinite(np.delete(out, 1, 0)))
 
 
 # ---- expert FFN --------------------------------------------------------------
