@@ -1,0 +1,422 @@
+// C ABI of the MoE layer forward (declarations and contracts: include/moe.h).
+//
+// This layer validates every host-visible argument before anything is
+// enqueued, carves the caller's workspace, and enqueues the kernels on the
+// caller's stream.  It allocates nothing and never synchronises, except in
+// moe_error.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cstring>
+
+#include "common.h"
+
+namespace rde {
+
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t ctrl, partial, lrank, rexp, mt_off, ids, w, counts, offsets, row_src, route_dst;
+    size_t x_disp, h, h_sh, ybuf, y_shared, total;
+};
+
+inline int64_t r_max_of(const moe_problem& p) {
+    const int64_t a = (int64_t)p.T * p.k, b = (int64_t)p.E * p.C;
+    return a < b ? a : b;
+}
+inline int act_bytes(const moe_problem& p) { return p.act_dtype == MOE_F32 ? 4 : 2; }
+inline int gemm_bm(const moe_problem& p) { return p.act_dtype == MOE_F32 ? kGemmF32BM : kGemmBM; }
+
+moe_status check_problem(const moe_problem* pp) {
+    if (!pp) return MOE_ERR_ARG;
+    const moe_problem& p = *pp;
+    if (p.T < 0 || p.H <= 0 || p.E <= 0 || p.k <= 0 || p.I <= 0 || p.C <= 0) return MOE_ERR_ARG;
+    if (p.k > 32 || p.k > p.E) return MOE_ERR_ARG;
+    if (p.act_dtype != MOE_F32 && p.act_dtype != MOE_BF16) return MOE_ERR_ARG;
+    if (p.w_dtype != MOE_F32 && p.w_dtype != MOE_BF16 && p.w_dtype != MOE_E4M3) return MOE_ERR_ARG;
+    if ((p.w_dtype == MOE_F32) != (p.act_dtype == MOE_F32)) return MOE_ERR_ARG;
+    if (p.act != MOE_SWIGLU && p.act != MOE_RELU2) return MOE_ERR_ARG;
+    if (p.renormalize != 0 && p.renormalize != 1) return MOE_ERR_ARG;
+    if (p.n_shared < 0 || p.n_shared > 8) return MOE_ERR_ARG;
+    if (p.n_shared > 0 && p.I_shared <= 0) return MOE_ERR_ARG;
+    if (p.E > 1024) return MOE_ERR_UNSUPPORTED;
+    if (p.H % 128 || p.I % 128) return MOE_ERR_UNSUPPORTED;
+    if (p.n_shared > 0 && p.I_shared % 128) return MOE_ERR_UNSUPPORTED;
+    const int64_t Q = (int64_t)p.T * p.k;
+    if (Q >= INT_MAX / 2) return MOE_ERR_UNSUPPORTED;  // route and row indices are int32
+    return MOE_OK;
+}
+
+Layout layout_of(const moe_problem& p) {
+    Layout L;
+    const int64_t Q = (int64_t)p.T * p.k, R = r_max_of(p);
+    const int nb = count_blocks(Q) > 0 ? count_blocks(Q) : 1;
+    const size_t ab = (size_t)act_bytes(p);
+    const int groups = p.E > p.n_shared ? p.E : p.n_shared;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o += up(bytes > 0 ? bytes : 1); return at; };
+    L.ctrl = take(sizeof(int32_t) * CTRL_WORDS);
+    L.partial = take(sizeof(int32_t) * (size_t)nb * p.E);
+    L.lrank = take(sizeof(int32_t) * (size_t)Q);
+    L.rexp = take(sizeof(int32_t) * (size_t)Q);
+    L.mt_off = take(sizeof(int32_t) * (size_t)(groups + 2));
+    L.ids = take(sizeof(int32_t) * (size_t)Q);
+    L.w = take(sizeof(float) * (size_t)Q);
+    L.counts = take(sizeof(int32_t) * (size_t)p.E);
+    L.offsets = take(sizeof(int32_t) * (size_t)(p.E + 1));
+    L.row_src = take(sizeof(int32_t) * (size_t)R);
+    L.route_dst = take(sizeof(int32_t) * (size_t)Q);
+    L.x_disp = take(ab * (size_t)R * p.H);
+    L.h = take(ab * (size_t)R * p.I);
+    L.h_sh = take(p.n_shared ? ab * (size_t)p.T * p.n_shared * p.I_shared : 0);
+    L.ybuf = take(ab * (size_t)Q * p.H);
+    L.y_shared = take(p.n_shared ? sizeof(float) * (size_t)p.T * p.H : 0);
+    L.total = o;
+    return L;
+}
+
+template <typename T_>
+T_* at(void* ws, size_t off) { return (T_*)((char*)ws + off); }
+
+inline bool aligned16(const void* q) { return ((uintptr_t)q & 15) == 0; }
+
+moe_status check_ws(const moe_problem& p, void* ws, size_t ws_bytes, Layout* L) {
+    if (!ws || ((uintptr_t)ws & (kAlign - 1))) return MOE_ERR_WORKSPACE;
+    *L = layout_of(p);
+    if (ws_bytes < L->total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int gemm_grid(int64_t tiles_upper) {
+    int g = device_cu_count() * 2;
+    g = (g + 7) / 8 * 8;
+    if (tiles_upper < g) g = (int)((tiles_upper + 7) / 8 * 8);
+    return g > 8 ? g : 8;
+}
+
+// GEMM1 (x_disp -> h) over the routed experts, tile table mt_off.
+hipError_t run_gemm1(const moe_problem& p, const void* x_disp, const int32_t* offsets,
+                     const int32_t* mt_off, const void* w13, const float* s13, void* h,
+                     hipStream_t s) {
+    GemmArgs a = {};
+    a.A = x_disp;
+    a.lda = p.H;
+    a.B = w13;
+    a.N_w = p.act == MOE_SWIGLU ? 2 * p.I : p.I;
+    a.b_group_stride = (int64_t)a.N_w * p.H;
+    a.b_seg_stride = 0;
+    a.k_seg = p.H;
+    a.bscale = s13;
+    a.K = p.H;
+    a.n_groups = p.E;
+    a.offsets = offsets;
+    a.mt_off = mt_off;
+    a.epi = p.act == MOE_SWIGLU ? EPI_SWIGLU : EPI_RELU2;
+    a.out = h;
+    a.ldo = p.I;
+    a.out_col_per_group = 0;
+    a.I = p.I;
+    const int64_t R = r_max_of(p);
+    if (p.act_dtype == MOE_F32) {
+        a.n_tiles = p.act == MOE_SWIGLU ? p.I / 32 : p.I / 64;
+        return launch_gemm_f32(a, gemm_grid((R / kGemmF32BM + p.E) * a.n_tiles), s);
+    }
+    a.n_tiles = p.act == MOE_SWIGLU ? p.I / 64 : p.I / 128;
+    return launch_gemm_bf16(a, p.w_dtype, gemm_grid((R / kGemmBM + p.E) * a.n_tiles), s);
+}
+
+// GEMM2 (h -> y) over the routed experts, epilogue EPI_STORE (y_disp) or
+// EPI_COMBINE (weighted rows into the token-ordered slot buffer).
+hipError_t run_gemm2(const moe_problem& p, const void* h, const int32_t* offsets,
+                     const int32_t* mt_off, const void* w2, const float* s2, int epi, void* out,
+                     const float* route_w, const int32_t* row_src, hipStream_t s) {
+    GemmArgs a = {};
+    a.A = h;
+    a.lda = p.I;
+    a.B = w2;
+    a.N_w = p.H;
+    a.b_group_stride = (int64_t)p.H * p.I;
+    a.k_seg = p.I;
+    a.bscale = s2;
+    a.K = p.I;
+    a.n_groups = p.E;
+    a.offsets = offsets;
+    a.mt_off = mt_off;
+    a.epi = epi;
+    a.out = out;
+    a.ldo = p.H;
+    a.route_w = route_w;
+    a.row_src = row_src;
+    a.I = p.I;
+    const int64_t R = r_max_of(p);
+    if (p.act_dtype == MOE_F32) {
+        a.n_tiles = p.H / 64;
+        return launch_gemm_f32(a, gemm_grid((R / kGemmF32BM + p.E) * a.n_tiles), s);
+    }
+    a.n_tiles = p.H / 128;
+    return launch_gemm_bf16(a, p.w_dtype, gemm_grid((R / kGemmBM + p.E) * a.n_tiles), s);
+}
+
+// Shared experts: h_sh [T, S*Is] = SwiGLU over every token for each expert s,
+// then y_shared [T, H] (float32) = h_sh @ [W2_0 | W2_1 | ...]^T as one
+// product whose K runs over the concatenated shared intermediates.
+hipError_t run_shared(const moe_problem& p, const void* x, const void* w13_sh, const void* w2_sh,
+                      void* h_sh, float* y_shared, hipStream_t s) {
+    const int S = p.n_shared, Is = p.I_shared;
+    const int wdt = p.act_dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
+    GemmArgs a = {};
+    a.A = x;
+    a.lda = p.H;
+    a.B = w13_sh;
+    a.N_w = 2 * Is;
+    a.b_group_stride = (int64_t)2 * Is * p.H;
+    a.k_seg = p.H;
+    a.K = p.H;
+    a.n_groups = S;
+    a.uniform_rows = p.T;
+    a.epi = EPI_SWIGLU;
+    a.out = h_sh;
+    a.ldo = (int64_t)S * Is;
+    a.out_col_per_group = Is;
+    a.I = Is;
+    hipError_t e;
+    const int bm = p.act_dtype == MOE_F32 ? kGemmF32BM : kGemmBM;
+    const int64_t mt = (int64_t)((p.T + bm - 1) / bm);
+    if (p.act_dtype == MOE_F32) {
+        a.n_tiles = Is / 32;
+        e = launch_gemm_f32(a, gemm_grid(mt * S * a.n_tiles), s);
+    } else {
+        a.n_tiles = Is / 64;
+        e = launch_gemm_bf16(a, wdt, gemm_grid(mt * S * a.n_tiles), s);
+    }
+    if (e != hipSuccess) return e;
+    GemmArgs b = {};
+    b.A = h_sh;
+    b.lda = (int64_t)S * Is;
+    b.B = w2_sh;
+    b.N_w = p.H;
+    b.b_group_stride = 0;
+    b.k_seg = Is;
+    b.b_seg_stride = (int64_t)p.H * Is;
+    b.K = S * Is;
+    b.n_groups = 1;
+    b.uniform_rows = p.T;
+    b.epi = EPI_F32;
+    b.out = y_shared;
+    b.ldo = p.H;
+    if (p.act_dtype == MOE_F32) {
+        b.n_tiles = p.H / 64;
+        return launch_gemm_f32(b, gemm_grid(mt * b.n_tiles), s);
+    }
+    b.n_tiles = p.H / 128;
+    return launch_gemm_bf16(b, wdt, gemm_grid(mt * b.n_tiles), s);
+}
+
+moe_status check_ptrs16(std::initializer_list<const void*> ps) {
+    for (const void* q : ps)
+        if (!q || !aligned16(q)) return MOE_ERR_ARG;
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace rde
+
+using namespace rde;
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported problem";
+        case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+moe_status moe_workspace_bytes(const moe_problem* p, size_t* bytes) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!bytes) return MOE_ERR_ARG;
+    *bytes = layout_of(*p).total;
+    return MOE_OK;
+}
+
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+    if (!ws || ((uintptr_t)ws & 255) || ws_bytes < sizeof(int32_t) * CTRL_WORDS) return MOE_ERR_WORKSPACE;
+    return hip_status(launch_fill_i32((int32_t*)ws, CTRL_WORDS, 0, (hipStream_t)stream));
+}
+
+moe_status moe_route(const moe_problem* p, const float* logits, int32_t* ids, float* w, void* ws,
+                     size_t ws_bytes, void* stream) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    Layout L;
+    if ((st = check_ws(*p, ws, ws_bytes, &L)) != MOE_OK) return st;
+    if (p->T == 0) return MOE_OK;
+    if (!logits || !ids || !w) return MOE_ERR_ARG;
+    return hip_status(launch_route(logits, p->T, p->E, p->k, p->renormalize, ids, w, (hipStream_t)stream));
+}
+
+moe_status moe_dispatch(const moe_problem* p, const void* x, const int32_t* ids, int32_t* counts,
+                        int32_t* offsets, int32_t* row_src, int32_t* route_dst, void* x_disp,
+                        void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    Layout L;
+    if ((st = check_ws(*p, ws, ws_bytes, &L)) != MOE_OK) return st;
+    if (!counts || !offsets) return MOE_ERR_ARG;
+    if (p->T > 0 && (check_ptrs16({x, x_disp}) != MOE_OK || !ids || !row_src || !route_dst))
+        return MOE_ERR_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_count_rank(ids, p->T, p->k, p->E, p->C, gemm_bm(*p), at<int32_t>(ws, L.rexp),
+                                     at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), counts,
+                                     offsets, at<int32_t>(ws, L.mt_off), at<int32_t>(ws, L.ctrl), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(launch_scatter(x, p->T, p->H, p->k, p->E, p->C, act_bytes(*p), r_max_of(*p),
+                                     at<int32_t>(ws, L.rexp), at<int32_t>(ws, L.lrank),
+                                     at<int32_t>(ws, L.partial), offsets, route_dst, row_src, x_disp, s));
+}
+
+moe_status moe_expert_ffn(const moe_problem* p, const void* x_disp, const int32_t* offsets,
+                          const void* w13, const void* w2, const float* s13, const float* s2,
+                          void* y_disp, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    Layout L;
+    if ((st = check_ws(*p, ws, ws_bytes, &L)) != MOE_OK) return st;
+    if (p->T == 0 || r_max_of(*p) == 0) return MOE_OK;
+    if (check_ptrs16({x_disp, w13, w2, y_disp}) != MOE_OK || !offsets) return MOE_ERR_ARG;
+    if ((p->w_dtype == MOE_E4M3) != (s13 != nullptr && s2 != nullptr)) return MOE_ERR_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t* mt = at<int32_t>(ws, L.mt_off);
+    if (launch_tile_table(offsets, p->E, p->C, gemm_bm(*p), mt, s) != hipSuccess) return MOE_ERR_HIP;
+    void* h = at<void>(ws, L.h);
+    if (run_gemm1(*p, x_disp, offsets, mt, w13, s13, h, s) != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(run_gemm2(*p, h, offsets, mt, w2, s2, EPI_STORE, y_disp, nullptr, nullptr, s));
+}
+
+moe_status moe_shared_ffn(const moe_problem* p, const void* x, const void* w13_sh, const void* w2_sh,
+                          float* y_shared, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    Layout L;
+    if ((st = check_ws(*p, ws, ws_bytes, &L)) != MOE_OK) return st;
+    if (p->n_shared == 0) return MOE_ERR_ARG;
+    if (p->T == 0) return MOE_OK;
+    if (check_ptrs16({x, w13_sh, w2_sh, y_shared}) != MOE_OK) return MOE_ERR_ARG;
+    return hip_status(run_shared(*p, x, w13_sh, w2_sh, at<void>(ws, L.h_sh), y_shared, (hipStream_t)stream));
+}
+
+moe_status moe_combine(const moe_problem* p, const void* y_disp, const int32_t* route_dst,
+                       const float* w, const float* y_shared, void* out, void* ws, size_t ws_bytes,
+                       void* stream) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    Layout L;
+    if ((st = check_ws(*p, ws, ws_bytes, &L)) != MOE_OK) return st;
+    if (p->T == 0) return MOE_OK;
+    if (check_ptrs16({out}) != MOE_OK || !route_dst || !w) return MOE_ERR_ARG;
+    if (r_max_of(*p) > 0 && check_ptrs16({y_disp}) != MOE_OK) return MOE_ERR_ARG;
+    if (y_shared && !aligned16(y_shared)) return MOE_ERR_ARG;
+    return hip_status(launch_combine(y_disp, 1, route_dst, w, y_shared, out, p->T, p->k, p->H,
+                                     p->act_dtype, (hipStream_t)stream));
+}
+
+moe_status moe_forward(const moe_problem* p, const void* x, const float* logits, const int32_t* ids_in,
+                       const float* w_in, const void* w13, const void* w2, const float* s13,
+                       const float* s2, const void* w13_sh, const void* w2_sh, void* out,
+                       const moe_meta* meta, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    Layout L;
+    if ((st = check_ws(*p, ws, ws_bytes, &L)) != MOE_OK) return st;
+    const moe_problem& P = *p;
+    const bool pre = ids_in != nullptr || w_in != nullptr;
+    if (pre && !(ids_in && w_in)) return MOE_ERR_ARG;
+    if (P.T > 0) {
+        if (check_ptrs16({x, w13, w2, out}) != MOE_OK) return MOE_ERR_ARG;
+        if (!pre && !logits) return MOE_ERR_ARG;
+        if ((P.w_dtype == MOE_E4M3) != (s13 != nullptr && s2 != nullptr)) return MOE_ERR_ARG;
+        if (P.n_shared && check_ptrs16({w13_sh, w2_sh}) != MOE_OK) return MOE_ERR_ARG;
+    }
+    moe_meta m = {};
+    if (meta) m = *meta;
+    int32_t* ids = m.ids ? m.ids : at<int32_t>(ws, L.ids);
+    float* w = m.w ? m.w : at<float>(ws, L.w);
+    int32_t* counts = m.counts ? m.counts : at<int32_t>(ws, L.counts);
+    int32_t* offsets = m.offsets ? m.offsets : at<int32_t>(ws, L.offsets);
+    int32_t* row_src = m.row_src ? m.row_src : at<int32_t>(ws, L.row_src);
+    int32_t* route_dst = m.route_dst ? m.route_dst : at<int32_t>(ws, L.route_dst);
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t Q = (int64_t)P.T * P.k;
+    hipError_t e = hipSuccess;
+    if (pre) {
+        // preselected routes: copy into the metadata outputs when they differ
+        if (ids != ids_in && Q) e = hipMemcpyAsync(ids, ids_in, sizeof(int32_t) * Q, hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess && w != w_in && Q)
+            e = hipMemcpyAsync(w, w_in, sizeof(float) * Q, hipMemcpyDeviceToDevice, s);
+    } else if (P.T > 0) {
+        e = launch_route(logits, P.T, P.E, P.k, P.renormalize, ids, w, s);
+    }
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    void* x_disp = at<void>(ws, L.x_disp);
+    int32_t* mt = at<int32_t>(ws, L.mt_off);
+    e = launch_count_rank(ids, P.T, P.k, P.E, P.C, gemm_bm(P), at<int32_t>(ws, L.rexp),
+                          at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), counts, offsets, mt,
+                          at<int32_t>(ws, L.ctrl), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (P.T == 0) return MOE_OK;
+    e = launch_scatter(x, P.T, P.H, P.k, P.E, P.C, act_bytes(P), r_max_of(P), at<int32_t>(ws, L.rexp),
+                       at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), offsets, route_dst, row_src,
+                       x_disp, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    void* h = at<void>(ws, L.h);
+    void* ybuf = at<void>(ws, L.ybuf);
+    float* y_sh = P.n_shared ? at<float>(ws, L.y_shared) : nullptr;
+    if (r_max_of(P) > 0) {
+        if (run_gemm1(P, x_disp, offsets, mt, w13, s13, h, s) != hipSuccess) return MOE_ERR_HIP;
+        if (run_gemm2(P, h, offsets, mt, w2, s2, EPI_COMBINE, ybuf, w, row_src, s) != hipSuccess)
+            return MOE_ERR_HIP;
+    }
+    if (P.n_shared && run_shared(P, x, w13_sh, w2_sh, at<void>(ws, L.h_sh), y_sh, s) != hipSuccess)
+        return MOE_ERR_HIP;
+    return hip_status(launch_combine(ybuf, 0, route_dst, nullptr, y_sh, out, P.T, P.k, P.H, P.act_dtype, s));
+}
+
+moe_status moe_error(void* ws, size_t ws_bytes, void* stream, int32_t* n_invalid_routes) {
+    if (!ws || ((uintptr_t)ws & 255) || ws_bytes < sizeof(int32_t) * CTRL_WORDS) return MOE_ERR_WORKSPACE;
+    if (!n_invalid_routes) return MOE_ERR_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t v = 0;
+    if (hipMemcpyAsync(&v, (int32_t*)ws + CTRL_BAD_ROUTES, sizeof v, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_fill_i32((int32_t*)ws + CTRL_BAD_ROUTES, 1, 0, s) != hipSuccess) return MOE_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+    *n_invalid_routes = v;
+    return MOE_OK;
+}
+
+}  // extern "C"

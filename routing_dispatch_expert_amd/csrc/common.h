@@ -1,0 +1,105 @@
+// Internal declarations of the gfx950 MoE library: vector types, small
+// device helpers and the kernel launchers called by the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace rde {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kWave = 64;
+
+// ---- workspace control words (first 256 bytes of ws) --------------------
+enum CtrlWord {
+    CTRL_BAD_ROUTES = 0,   // malformed routes seen since the last moe_error
+    CTRL_TICKET = 1,       // arrival counter of the count kernel's blocks
+    CTRL_WORDS = 64
+};
+
+// ---- count-first dispatch ------------------------------------------------
+// Routes per block of the count/rank kernel: 4 waves x 8 routes per lane.
+constexpr int kCountWaves = 4;
+constexpr int kCountPerLane = 8;
+constexpr int kCountBlock = kWave * kCountWaves * kCountPerLane;   // 2048
+
+inline int count_blocks(int64_t Q) { return (int)((Q + kCountBlock - 1) / kCountBlock); }
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int renorm,
+                        int32_t* ids, float* w, hipStream_t s);
+
+// ids -> rexp (validated expert or -2), lrank (rank inside its block),
+// partial (per-block counts, turned into per-block bases by the last block),
+// counts, offsets and the m-tile table of the grouped GEMM (tile rows bm).
+hipError_t launch_count_rank(const int32_t* ids, int T, int k, int E, int C, int bm,
+                             int32_t* rexp, int32_t* lrank, int32_t* partial,
+                             int32_t* counts, int32_t* offsets, int32_t* mt_off,
+                             int32_t* ctrl, hipStream_t s);
+
+// route_dst, row_src and the x -> x_disp row copies.
+hipError_t launch_scatter(const void* x, int T, int H, int k, int E, int C, int elem_bytes,
+                          int64_t r_max, const int32_t* rexp, const int32_t* lrank,
+                          const int32_t* base, const int32_t* offsets,
+                          int32_t* route_dst, int32_t* row_src, void* x_disp, hipStream_t s);
+
+// offsets -> m-tile table (for moe_expert_ffn, whose caller passes offsets only).
+hipError_t launch_tile_table(const int32_t* offsets, int E, int C, int bm, int32_t* mt_off,
+                             hipStream_t s);
+
+// ---- grouped GEMM ------------------------------------------------------------
+enum Epilogue {
+    EPI_SWIGLU = 0,   // out[row, col] = act dtype of silu(gate) * up
+    EPI_RELU2 = 1,    // out[row, col] = act dtype of max(acc, 0)^2
+    EPI_STORE = 2,    // out[row, col] = act dtype of acc
+    EPI_COMBINE = 3,  // out[row_src[row], col] = act dtype of w[row_src[row]] * acc
+    EPI_F32 = 4       // out[row, col] = float acc (shared-expert sum)
+};
+
+struct GemmArgs {
+    const void* A;          // activations, rows of lda elements (act dtype)
+    int64_t lda;
+    const void* B;          // weights [n_groups][N_w][K] (w dtype)
+    int64_t b_group_stride; // elements between groups (experts)
+    int64_t b_seg_stride;   // elements between K segments (concatenated shared experts)
+    int k_seg;              // K-segment length (== K when B is not segmented)
+    const float* bscale;    // e4m3 per-row scales [n_groups][N_w] or null
+    int K;
+    int N_w;                // rows of B per group
+    int n_tiles;            // column tiles per m-tile
+    int n_groups;
+    const int32_t* offsets; // [n_groups+1] first A row of each group; null = uniform
+    const int32_t* mt_off;  // [n_groups+1] m-tile prefix; null = uniform
+    int uniform_rows;       // rows per group when offsets is null (A rows shared)
+    int epi;
+    void* out;
+    int64_t ldo;
+    int64_t out_col_per_group;  // column offset added per group (concatenated h)
+    const float* route_w;       // EPI_COMBINE
+    const int32_t* row_src;     // EPI_COMBINE
+    int I;                      // EPI_SWIGLU: up rows start at I in B
+};
+
+constexpr int kGemmBM = 128;   // rows per m-tile of the bf16 MFMA kernel
+constexpr int kGemmF32BM = 64; // rows per m-tile of the f32 kernel
+
+hipError_t launch_gemm_bf16(const GemmArgs& a, int w_dtype, int grid, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmArgs& a, int grid, hipStream_t s);
+
+// ---- combine -----------------------------------------------------------------
+// out[t] = sum_j (route_dst >= 0) coef * y[src] (+ y_shared[t]); NaN row when a
+// route of t is malformed.  gather: src = route_dst[q], coef = w[q];
+// slots: src = q, coef = 1 (the weights were applied in the GEMM epilogue).
+hipError_t launch_combine(const void* y, int gather, const int32_t* route_dst, const float* w,
+                          const float* y_shared, void* out, int T, int k, int H, int act_dtype,
+                          hipStream_t s);
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace rde

@@ -1,0 +1,278 @@
+// Count-first token dispatch (afdEP count-first validation record: count the
+// routes per expert first, then compute the prefix sums, then stream every
+// row to its known offset in an expert-contiguous buffer of capacity C rows
+// per expert).
+//
+// Kernel 1, count_rank: blocks of 2048 routes (4 waves x 8 routes per lane,
+// each wave a contiguous run).  For every 64-route step a wave finds the
+// lanes holding the same expert by ballots over the bits of the expert id;
+// a lane's stable rank is its wave's running LDS count for that expert plus
+// the number of lower lanes in its group, and the group's lowest lane adds
+// the group size.  Per-wave counts are then prefix-summed over the block's
+// waves (giving the rank of a route among the block's routes of its expert)
+// and the block totals are published.  The last block to arrive (atomic
+// ticket) turns the per-block totals into per-block bases, writes the raw
+// counts, the exclusive scan of min(count, C) and the m-tile table of the
+// grouped GEMM, and resets the ticket.
+//
+// Kernel 2, scatter: one block per token.  Each route's final rank is
+// base[block][e] + its in-block rank; a rank below C places the route at row
+// offsets[e] + rank.  The token's row is read once and stored to each of its
+// kept rows with 16-byte vector stores.
+#include "common.h"
+
+namespace rde {
+namespace {
+
+constexpr int kScanThreads = 256;
+
+// Block-wide exclusive scan of up to kScanThreads * per-thread values held in
+// LDS array `v` (n entries, in place); returns the total.  Two arrays at once.
+__device__ void block_scan2(int32_t* a, int32_t* b, int n, int32_t* tot_a, int32_t* tot_b) {
+    __shared__ int32_t sa[kScanThreads], sb[kScanThreads];
+    const int tid = threadIdx.x;
+    const int per = (n + kScanThreads - 1) / kScanThreads;
+    const int lo = tid * per, hi = min(n, lo + per);
+    int32_t ra = 0, rb = 0;
+    for (int i = lo; i < hi; ++i) {
+        ra += a[i];
+        rb += b[i];
+    }
+    sa[tid] = ra;
+    sb[tid] = rb;
+    __syncthreads();
+    for (int off = 1; off < kScanThreads; off <<= 1) {
+        int32_t xa = tid >= off ? sa[tid - off] : 0;
+        int32_t xb = tid >= off ? sb[tid - off] : 0;
+        __syncthreads();
+        sa[tid] += xa;
+        sb[tid] += xb;
+        __syncthreads();
+    }
+    int32_t ea = sa[tid] - ra, eb = sb[tid] - rb;  // exclusive prefix of this thread's run
+    for (int i = lo; i < hi; ++i) {
+        int32_t ta = a[i], tb = b[i];
+        a[i] = ea;
+        b[i] = eb;
+        ea += ta;
+        eb += tb;
+    }
+    if (tid == kScanThreads - 1) {
+        *tot_a = sa[tid];
+        *tot_b = sb[tid];
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void count_rank_kernel(
+    const int32_t* __restrict__ ids, int64_t Q, int k, int E, int ebits, int C, int bm,
+    int32_t* __restrict__ rexp, int32_t* __restrict__ lrank, int32_t* __restrict__ partial,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ mt_off,
+    int32_t* __restrict__ ctrl) {
+    extern __shared__ int32_t lds[];  // [kCountWaves][E] during counting; [2][E] in the scan
+    __shared__ int s_last;
+    __shared__ int32_t s_tot[2];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    for (int i = tid; i < kCountWaves * E; i += blockDim.x) lds[i] = 0;
+    __syncthreads();
+
+    int32_t* hist = lds + wv * E;
+    const int64_t q0 = (int64_t)blockIdx.x * kCountBlock + (int64_t)wv * (kWave * kCountPerLane);
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int rank_w[kCountPerLane], ex[kCountPerLane];
+    int n_bad = 0;
+#pragma unroll
+    for (int it = 0; it < kCountPerLane; ++it) {
+        const int64_t q = q0 + it * kWave + lane;
+        int e = -1;
+        if (q < Q) {
+            e = ids[q];
+            bool ok = (e >= 0 && e < E);
+            const int64_t t = q / k;
+            const int j = (int)(q - t * k);
+            for (int jj = 0; ok && jj < j; ++jj) ok = (ids[t * k + jj] != e);
+            if (!ok) {
+                e = -2;
+                ++n_bad;
+            }
+            rexp[q] = e;
+        }
+        const bool valid = e >= 0;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < ebits; ++b) {
+            const bool bit = valid && ((e >> b) & 1);
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        int r = 0;
+        if (valid) {
+            const int before = __popcll(peers & lt);
+            r = hist[e] + before;          // every lane reads before any lane writes
+            if (before == 0) hist[e] += __popcll(peers);
+        }
+        rank_w[it] = r;
+        ex[it] = e;
+    }
+    // malformed routes: one atomic per wave
+    const uint64_t badm = __ballot(n_bad > 0);
+    int wave_bad = n_bad;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wave_bad += __shfl_xor(wave_bad, off, kWave);
+    if (badm && lane == 0) atomicAdd(&ctrl[CTRL_BAD_ROUTES], wave_bad);
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) {
+        int32_t run = 0;
+        for (int w = 0; w < kCountWaves; ++w) {
+            const int32_t c = lds[w * E + e];
+            lds[w * E + e] = run;
+            run += c;
+        }
+        partial[(int64_t)blockIdx.x * E + e] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < kCountPerLane; ++it) {
+        const int64_t q = q0 + it * kWave + lane;
+        if (q < Q) lrank[q] = ex[it] >= 0 ? hist[ex[it]] + rank_w[it] : -1;
+    }
+
+    // ---- last block: per-block bases, counts, offsets, m-tile table ----
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = (atomicAdd(&ctrl[CTRL_TICKET], 1) == (int)gridDim.x - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    int32_t* kept = lds;
+    int32_t* tiles = lds + E;
+    const int nb = gridDim.x;
+    for (int e = tid; e < E; e += blockDim.x) {
+        int32_t run = 0;
+        for (int b = 0; b < nb; ++b) {
+            int32_t* p = &partial[(int64_t)b * E + e];
+            const int32_t c = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *p = run;
+            run += c;
+        }
+        counts[e] = run;
+        const int32_t kp = run < C ? run : C;
+        kept[e] = kp;
+        tiles[e] = (kp + bm - 1) / bm;
+    }
+    __syncthreads();
+    block_scan2(kept, tiles, E, &s_tot[0], &s_tot[1]);
+    for (int e = tid; e < E; e += blockDim.x) {
+        offsets[e] = kept[e];
+        mt_off[e] = tiles[e];
+    }
+    if (tid == 0) {
+        offsets[E] = s_tot[0];
+        mt_off[E] = s_tot[1];
+        ctrl[CTRL_TICKET] = 0;
+    }
+}
+
+__global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets, int E,
+                                                         int bm, int32_t* __restrict__ mt_off) {
+    extern __shared__ int32_t lds[];
+    __shared__ int32_t s_tot[2];
+    int32_t* tiles = lds;
+    int32_t* dummy = lds + E;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const int32_t kp = offsets[e + 1] - offsets[e];
+        tiles[e] = (kp + bm - 1) / bm;
+        dummy[e] = 0;
+    }
+    __syncthreads();
+    block_scan2(tiles, dummy, E, &s_tot[0], &s_tot[1]);
+    for (int e = threadIdx.x; e < E; e += blockDim.x) mt_off[e] = tiles[e];
+    if (threadIdx.x == 0) mt_off[E] = s_tot[0];
+}
+
+template <typename V>
+__global__ __launch_bounds__(256) void scatter_kernel(
+    const V* __restrict__ x, int H_vec, int k, int E, int C, int64_t r_max,
+    const int32_t* __restrict__ rexp, const int32_t* __restrict__ lrank,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ route_dst, int32_t* __restrict__ row_src, V* __restrict__ x_disp) {
+    __shared__ int32_t s_row[32];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    if (tid < k) {
+        const int64_t q = (int64_t)t * k + tid;
+        const int e = rexp[q];
+        int32_t row;
+        if (e < 0) {
+            row = -2;
+        } else {
+            const int32_t r = base[(q / kCountBlock) * E + e] + lrank[q];
+            row = r < C ? offsets[e] + r : -1;
+            if (row >= 0) row_src[row] = (int32_t)q;
+        }
+        route_dst[q] = row;
+        s_row[tid] = row;
+    }
+    // rows R .. r_max-1 of row_src are unused: -1 (grid-stride over all blocks)
+    const int64_t R = offsets[E];
+    for (int64_t r = R + (int64_t)blockIdx.x * blockDim.x + tid; r < r_max;
+         r += (int64_t)gridDim.x * blockDim.x)
+        row_src[r] = -1;
+    __syncthreads();
+    const V* src = x + (int64_t)t * H_vec;
+    for (int c = tid; c < H_vec; c += blockDim.x) {
+        const V v = src[c];
+        for (int j = 0; j < k; ++j) {
+            const int32_t row = s_row[j];
+            if (row >= 0) x_disp[(int64_t)row * H_vec + c] = v;
+        }
+    }
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_count_rank(const int32_t* ids, int T, int k, int E, int C, int bm, int32_t* rexp,
+                             int32_t* lrank, int32_t* partial, int32_t* counts, int32_t* offsets,
+                             int32_t* mt_off, int32_t* ctrl, hipStream_t s) {
+    const int64_t Q = (int64_t)T * k;
+    const int nb = count_blocks(Q) > 0 ? count_blocks(Q) : 1;
+    int ebits = 1;
+    while ((1 << ebits) < E) ++ebits;
+    const size_t lds = sizeof(int32_t) * (size_t)kCountWaves * E;
+    hipLaunchKernelGGL(count_rank_kernel, dim3(nb), dim3(kWave * kCountWaves), lds, s, ids, Q, k, E,
+                       ebits, C, bm, rexp, lrank, partial, counts, offsets, mt_off, ctrl);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_table(const int32_t* offsets, int E, int C, int bm, int32_t* mt_off,
+                             hipStream_t s) {
+    (void)C;
+    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(256), sizeof(int32_t) * 2 * (size_t)E, s,
+                       offsets, E, bm, mt_off);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter(const void* x, int T, int H, int k, int E, int C, int elem_bytes,
+                          int64_t r_max, const int32_t* rexp, const int32_t* lrank,
+                          const int32_t* base, const int32_t* offsets, int32_t* route_dst,
+                          int32_t* row_src, void* x_disp, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const int H_vec = (int)((int64_t)H * elem_bytes / 16);  // H*elem_bytes is a multiple of 256
+    hipLaunchKernelGGL(scatter_kernel<uint4>, dim3(T), dim3(256), 0, s, (const uint4*)x, H_vec, k, E,
+                       C, r_max, rexp, lrank, base, offsets, route_dst, row_src, (uint4*)x_disp);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+}  // namespace rde

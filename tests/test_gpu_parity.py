@@ -1,0 +1,409 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Each test prints the case it runs before touching the GPU.  Small cases are
+compared element by element against the full oracle; they span several
+128-row m-tiles with a ragged last tile, several k-tiles and n-tiles.  The
+full-size workloads (the pages' shapes) are compared bit-exactly on all
+routing / dispatch metadata and on sampled token rows for the FFN outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routing_dispatch_expert_amd as rde
+import synth
+from gpu_helpers import (DEV, act_dtype, assert_bf16_close, assert_close, assert_f32_close,
+                         np_i32, oracle_shared, oracle_token_rows, problem, r_max, workspace)
+
+pytestmark = pytest.mark.gpu
+
+# Small cases: the whole oracle finishes in seconds.
+SMALL = {
+    "tiny_fp32": ("tiny_fp32", {}),
+    "multi_tile_swiglu": ("prefill_T256", dict(T=600, H=256, E=4, k=2, I=256, C=600)),
+    "ragged_skew_capacity": ("skewed_bf16", dict(T=777, H=256, E=16, k=4, I=128, C=100)),
+    "relu2_small": ("relu2_distinct_R8", dict(H=256, I=256)),
+    "decode_shared_small": ("decode_T8", dict(T=37, H=256, I=128, I_shared=256, C=37)),
+    "fp8_small": ("skewed_fp8", dict(T=300, H=256, E=8, I=256, C=96)),
+    "k1_e1": ("prefill_T256", dict(T=130, H=128, E=1, k=1, I=128, C=130)),
+    "fp32_relu2_renorm": ("tiny_fp32", dict(act=synth.ACT_RELU2, renormalize=1, T=100, C=40)),
+}
+# Full-size workloads.
+FULL = ["tiny_fp32", "prefill_T256", "prefill_T2048", "prefill_T8192", "decode_T1", "decode_T8",
+        "decode_T32", "relu2_distinct_R1", "relu2_shared_R1", "relu2_distinct_R8",
+        "relu2_shared_R8", "relu2_distinct_R16", "relu2_shared_R16", "skewed_bf16", "skewed_fp8"]
+
+
+def _case(key):
+    if key in SMALL:
+        name, over = SMALL[key]
+        return synth.case(name, **over)
+    return synth.case(key)
+
+
+def _say(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+# ---- routing -----------------------------------------------------------------
+
+def _route_gpu(cs, logits_dev):
+    p = problem(cs)
+    ws = workspace(p)
+    ids = torch.empty((cs.T, cs.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((cs.T, cs.k), dtype=torch.float32, device=DEV)
+    rde.moe_route(p, logits_dev, ids, w, ws)
+    torch.cuda.synchronize()
+    return ids, w
+
+
+def _check_route(cs, logits):
+    ids, w = _route_gpu(cs, logits.to(DEV))
+    oi, ow = oracle.route(logits.numpy(), cs.k, cs.renormalize)
+    np.testing.assert_array_equal(np_i32(ids), oi)
+    assert_f32_close(w, ow, "w")
+    return ids, w, oi, ow
+
+
+@pytest.mark.parametrize("key", list(SMALL) + FULL)
+def test_route(key):
+    cs = _case(key)
+    _say("route", key, cs.T, cs.E, cs.k)
+    _check_route(cs, synth.make_logits(cs))
+
+
+def test_route_pm16_bit_exact():
+    for key in ("relu2_distinct_R16", "relu2_shared_R16"):
+        cs = synth.case(key)
+        _say("route pm16", key)
+        ids, w, oi, _ = _check_route(cs, synth.make_logits(cs))
+        # +16 / -16: every selected weight is exactly fl32(1/9)
+        assert torch.all(w.cpu() == torch.tensor(1.0, dtype=torch.float32) / 9)
+
+
+@pytest.mark.parametrize("E,k", [(7, 3), (64, 6), (200, 9), (1024, 32)])
+def test_route_ties_and_special_values(E, k):
+    _say("route ties", E, k)
+    g = torch.Generator().manual_seed(E)
+    pool = torch.tensor([-1.0, -0.0, 0.0, 1.0, 2.5, float("-inf"), float("nan")])
+    T = 300
+    lg = pool[torch.randint(0, len(pool), (T, E), generator=g)]
+    lg[0] = float("-inf")             # all -inf: NaN weights, lowest indices
+    lg[1] = torch.arange(E, dtype=torch.float32)
+    cs = synth.Case("ties", T=T, H=128, E=E, k=k, I=128, C=T)
+    ids, w = _route_gpu(cs, lg.to(DEV))
+    oi, ow = oracle.route(lg.numpy(), k)
+    np.testing.assert_array_equal(np_i32(ids), oi)
+    assert_f32_close(w, ow, "w")
+
+
+# ---- dispatch ----------------------------------------------------------------
+
+def _dispatch_gpu(cs, x_dev, ids_dev):
+    p = problem(cs)
+    ws = workspace(p)
+    R = r_max(cs)
+    counts = torch.empty(cs.E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(cs.E + 1, dtype=torch.int32, device=DEV)
+    row_src = torch.full((max(R, 1),), 12345, dtype=torch.int32, device=DEV)
+    route_dst = torch.empty((cs.T, cs.k), dtype=torch.int32, device=DEV)
+    x_disp = torch.zeros((max(R, 1), cs.H), dtype=act_dtype(cs), device=DEV)
+    rde.moe_dispatch(p, x_dev, ids_dev, counts, offsets, row_src, route_dst, x_disp, ws)
+    n_bad = rde.moe_error(ws)
+    return dict(counts=counts, offsets=offsets, row_src=row_src[:R], route_dst=route_dst,
+                x_disp=x_disp, n_bad=n_bad)
+
+
+def _check_dispatch(cs, x, ids_np):
+    g = _dispatch_gpu(cs, x.to(DEV), torch.from_numpy(ids_np).to(DEV))
+    d = oracle.dispatch(ids_np, cs.E, cs.C)
+    for key in ("counts", "offsets", "row_src", "route_dst"):
+        np.testing.assert_array_equal(np_i32(g[key]), d[key], err_msg=key)
+    assert g["n_bad"] == d["n_bad"]
+    R = int(d["offsets"][-1])
+    xo = oracle.gather_rows(oracle.from_torch(x), d["row_src"], R, cs.k)
+    xg = oracle.from_torch(g["x_disp"][:R].cpu())
+    assert np.array_equal(xg.view(np.uint8), xo.view(np.uint8)), "x_disp differs"
+    return d
+
+
+@pytest.mark.parametrize("key", list(SMALL) + FULL)
+def test_dispatch(key):
+    cs = _case(key)
+    _say("dispatch", key, cs.T, cs.E, cs.k, cs.C)
+    ids, _ = oracle.route(synth.make_logits(cs).numpy(), cs.k)
+    d = _check_dispatch(cs, synth.make_x(cs), ids)
+    assert d["counts"].sum() == cs.T * cs.k
+
+
+@pytest.mark.parametrize("kind", ["negative", "wide", "duplicate"])
+def test_dispatch_malformed_routes(kind):
+    _say("dispatch malformed", kind)
+    cs = synth.Case("bad", T=40, H=256, E=16, k=4, I=128, C=40)
+    ids = synth.bad_routes(cs.T, cs.k, cs.E, kind).numpy()
+    d = _check_dispatch(cs, synth.make_x(cs), ids)
+    assert d["n_bad"] == 1
+
+
+def test_dispatch_ragged_blocks_and_max_k():
+    # route counts around the 2048-route block boundary, k = 32, E = 1024
+    for T, E, k, C in ((2049 // 8 + 1, 128, 8, 7), (64, 1024, 32, 3), (4097, 33, 1, 4097)):
+        _say("dispatch ragged", T, E, k, C)
+        cs = synth.Case("rag", T=T, H=128, E=E, k=k, I=128, C=C, seed=T)
+        ids, _ = oracle.route(synth.make_logits(cs).numpy(), k)
+        _check_dispatch(cs, synth.make_x(cs), ids)
+
+
+# ---- expert FFN ----------------------------------------------------------------
+
+def _expert_ffn_gpu(cs, inp_dev, x_disp_dev, offsets_dev):
+    p = problem(cs)
+    ws = workspace(p)
+    R = r_max(cs)
+    y = torch.full((max(R, 1), cs.H), float("nan"), dtype=act_dtype(cs), device=DEV)
+    rde.moe_expert_ffn(p, x_disp_dev, offsets_dev, inp_dev.w13, inp_dev.w2, inp_dev.s13,
+                       inp_dev.s2, y, ws)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("key", list(SMALL) + ["prefill_T2048", "decode_T32", "relu2_shared_R16",
+                                               "skewed_fp8"])
+def test_expert_ffn(key):
+    cs = _case(key)
+    _say("expert_ffn", key)
+    inp_dev = synth.make_inputs(cs, DEV)
+    ids, _ = oracle.route(oracle.from_torch(inp_dev.logits), cs.k)
+    d = oracle.dispatch(ids, cs.E, cs.C)
+    R = int(d["offsets"][-1])
+    xh = oracle.from_torch(inp_dev.x)
+    xd = oracle.gather_rows(xh, d["row_src"], R, cs.k)
+    xd_dev = torch.from_numpy(xd.view(np.int16) if xd.dtype == np.uint16 else xd).to(DEV)
+    if xd.dtype == np.uint16:
+        xd_dev = xd_dev.view(torch.bfloat16)
+    y = _expert_ffn_gpu(cs, inp_dev, xd_dev, torch.from_numpy(d["offsets"]).to(DEV))
+    small = key in SMALL
+    for e in range(cs.E):
+        a, b = int(d["offsets"][e]), int(d["offsets"][e + 1])
+        if a == b:
+            continue
+        rows = list(range(a, b)) if small else sorted({a, b - 1, (a + b) // 2})
+        w13 = oracle.from_torch(inp_dev.w13[e])
+        w2 = oracle.from_torch(inp_dev.w2[e])
+        s13 = None if inp_dev.s13 is None else oracle.from_torch(inp_dev.s13[e])
+        s2 = None if inp_dev.s2 is None else oracle.from_torch(inp_dev.s2[e])
+        ref = oracle.expert_rows(xd[rows], w13, w2, cs.act, s13, s2)
+        assert_close(cs, y[rows], ref, f"y_disp expert {e}")
+        if not small and e > 24:
+            break
+
+
+def test_shared_ffn():
+    for key in ("decode_T1", "decode_T32", "decode_shared_small"):
+        cs = _case(key)
+        _say("shared_ffn", key)
+        inp_dev = synth.make_inputs(cs, DEV)
+        p = problem(cs)
+        ws = workspace(p)
+        ysh = torch.empty((cs.T, cs.H), dtype=torch.float32, device=DEV)
+        rde.moe_shared_ffn(p, inp_dev.x, inp_dev.w13_sh, inp_dev.w2_sh, ysh, ws)
+        torch.cuda.synchronize()
+        host = oracle.inputs_numpy(inp_dev.to("cpu"))
+        tokens = list(range(cs.T))
+        assert_bf16_close(ysh, oracle_shared(cs, host, tokens), "y_shared")
+
+
+# ---- combine -------------------------------------------------------------------
+
+@pytest.mark.parametrize("key", ["tiny_fp32", "ragged_skew_capacity", "decode_shared_small",
+                                 "prefill_T2048"])
+def test_combine(key):
+    cs = _case(key)
+    _say("combine", key)
+    ids, w = oracle.route(synth.make_logits(cs).numpy(), cs.k)
+    d = oracle.dispatch(ids, cs.E, cs.C)
+    R = max(int(d["offsets"][-1]), 1)
+    g = torch.Generator().manual_seed(3)
+    y32 = torch.randn((R, cs.H), generator=g)
+    y = y32.to(act_dtype(cs))
+    ysh = torch.randn((cs.T, cs.H), generator=g) if cs.n_shared else None
+    p = problem(cs)
+    ws = workspace(p)
+    out = torch.empty((cs.T, cs.H), dtype=act_dtype(cs), device=DEV)
+    w32 = torch.from_numpy(w.astype(np.float32))
+    rde.moe_combine(p, y.to(DEV), torch.from_numpy(d["route_dst"]).to(DEV), w32.to(DEV),
+                    None if ysh is None else ysh.to(DEV), out, ws)
+    torch.cuda.synchronize()
+    ref = oracle.combine(d["route_dst"], w32.double().numpy(), y.double().numpy(),
+                         None if ysh is None else ysh.double().numpy())
+    assert_close(cs, out, ref, "out")
+
+
+# ---- whole layer -----------------------------------------------------------------
+
+def _forward_gpu(cs, inp_dev, ids_in=None, w_in=None, with_meta=True):
+    p = problem(cs)
+    ws = workspace(p)
+    R = r_max(cs)
+    out = torch.empty((cs.T, cs.H), dtype=act_dtype(cs), device=DEV)
+    meta = None
+    if with_meta:
+        meta = dict(ids=torch.empty((cs.T, cs.k), dtype=torch.int32, device=DEV),
+                    w=torch.empty((cs.T, cs.k), dtype=torch.float32, device=DEV),
+                    counts=torch.empty(cs.E, dtype=torch.int32, device=DEV),
+                    offsets=torch.empty(cs.E + 1, dtype=torch.int32, device=DEV),
+                    row_src=torch.empty(max(R, 1), dtype=torch.int32, device=DEV),
+                    route_dst=torch.empty((cs.T, cs.k), dtype=torch.int32, device=DEV))
+    rde.moe_forward(p, inp_dev.x, inp_dev.logits, ids_in, w_in, inp_dev.w13, inp_dev.w2,
+                    inp_dev.s13, inp_dev.s2, inp_dev.w13_sh, inp_dev.w2_sh, out, meta, ws)
+    n_bad = rde.moe_error(ws)
+    return out, meta, n_bad
+
+
+def _check_meta(cs, meta, r):
+    np.testing.assert_array_equal(np_i32(meta["ids"]), r["ids"])
+    assert_f32_close(meta["w"], r["w"], "w")
+    for key in ("counts", "offsets", "route_dst"):
+        np.testing.assert_array_equal(np_i32(meta[key]), r[key], err_msg=key)
+    np.testing.assert_array_equal(np_i32(meta["row_src"])[:len(r["row_src"])], r["row_src"])
+
+
+@pytest.mark.parametrize("key", list(SMALL))
+def test_forward_small(key):
+    cs = _case(key)
+    _say("forward small", key)
+    inp_dev = synth.make_inputs(cs, DEV)
+    out, meta, n_bad = _forward_gpu(cs, inp_dev)
+    r = oracle.forward(cs, **oracle.inputs_numpy(inp_dev.to("cpu")))
+    _check_meta(cs, meta, r)
+    assert n_bad == 0
+    assert_close(cs, out, r["out"], "out")
+
+
+@pytest.mark.parametrize("key", FULL)
+def test_forward_full_size(key):
+    cs = synth.case(key)
+    _say("forward full", key)
+    inp_dev = synth.make_inputs(cs, DEV)
+    out, meta, _ = _forward_gpu(cs, inp_dev)
+    logits = oracle.from_torch(inp_dev.logits)
+    ids, w = oracle.route(logits, cs.k, cs.renormalize)
+    d = oracle.dispatch(ids, cs.E, cs.C)
+    r = dict(ids=ids, w=w, **d)
+    _check_meta(cs, meta, r)
+    rng = np.random.default_rng(0)
+    n_sample = {"skewed_bf16": 4, "skewed_fp8": 4}.get(key, 12)
+    tokens = sorted(set(rng.choice(cs.T, size=min(n_sample, cs.T), replace=False).tolist())
+                    | {0, cs.T - 1})
+    if key.startswith("skewed"):
+        dropped = np.nonzero((d["route_dst"] < 0).any(axis=1))[0]
+        if len(dropped):
+            tokens = sorted(set(tokens) | {int(dropped[-1])})
+    xh = oracle.from_torch(inp_dev.x)
+    host_sh = None
+    if cs.n_shared:
+        host_sh = oracle_shared(cs, dict(x=xh, w13_sh=oracle.from_torch(inp_dev.w13_sh),
+                                         w2_sh=oracle.from_torch(inp_dev.w2_sh)), tokens)
+    ref = oracle_token_rows(cs, inp_dev, xh, ids, w, d["route_dst"], tokens, None)
+    if host_sh is not None:
+        ref = ref + host_sh
+    assert_close(cs, out[tokens], ref, f"out rows {tokens}")
+
+
+def test_forward_preselected_is_bitwise_internal():
+    # the same routes given as preselected ids / weights give bitwise the
+    # same layer output (PR 33963: all outputs bitwise equal across the two
+    # routing modes on identical routes)
+    for key in ("relu2_distinct_R16", "multi_tile_swiglu", "tiny_fp32"):
+        cs = _case(key)
+        _say("preselected bitwise", key)
+        inp_dev = synth.make_inputs(cs, DEV)
+        out1, meta, _ = _forward_gpu(cs, inp_dev)
+        out2, _, _ = _forward_gpu(cs, inp_dev, meta["ids"].clone(), meta["w"].clone())
+        assert torch.equal(out1.view(torch.int16) if out1.dtype == torch.bfloat16 else out1.view(torch.int32),
+                           out2.view(torch.int16) if out2.dtype == torch.bfloat16 else out2.view(torch.int32))
+
+
+def test_forward_deterministic_and_batch_invariant():
+    cs = _case("multi_tile_swiglu")
+    _say("determinism / batch invariance")
+    inp_dev = synth.make_inputs(cs, DEV)
+    a, _, _ = _forward_gpu(cs, inp_dev, with_meta=False)
+    b, _, _ = _forward_gpu(cs, inp_dev, with_meta=False)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # capacity >= T*k: a sub-batch gives bitwise the same rows
+    sub = list(range(100, 160))
+    cs2 = synth.replace(cs, T=len(sub), C=len(sub) * cs.k)
+    inp2 = synth.Inputs(cs2, inp_dev.x[sub].contiguous(), inp_dev.logits[sub].contiguous(),
+                        inp_dev.w13, inp_dev.w2)
+    c, _, _ = _forward_gpu(cs2, inp2, with_meta=False)
+    assert torch.equal(c.view(torch.int16), a[sub].view(torch.int16))
+
+
+@pytest.mark.parametrize("kind", ["negative", "wide", "duplicate"])
+def test_forward_malformed_routes_poison_only_their_token(kind):
+    cs = synth.case("prefill_T256", T=24, H=256, E=16, k=4, I=128, C=24)
+    _say("forward malformed", kind)
+    inp_dev = synth.make_inputs(cs, DEV)
+    ids = synth.bad_routes(cs.T, cs.k, cs.E, kind)
+    w = torch.full((cs.T, cs.k), 0.25)
+    out, meta, n_bad = _forward_gpu(cs, inp_dev, ids.to(DEV), w.to(DEV))
+    assert n_bad == 1
+    r = oracle.forward(cs, **oracle.inputs_numpy(inp_dev.to("cpu")), ids_in=ids.numpy(),
+                       w_in=w.double().numpy())
+    np.testing.assert_array_equal(np_i32(meta["route_dst"]), r["route_dst"])
+    o = out.float().cpu()
+    assert torch.isnan(o[1]).all() and torch.isfinite(o[[0] + list(range(2, cs.T))]).all()
+    assert_close(cs, out, r["out"], "out")
+
+
+def test_forward_empty_batch():
+    cs = synth.case("prefill_T256", T=0, H=256, E=16, I=128)
+    _say("forward empty")
+    p = problem(cs)
+    ws = workspace(p)
+    counts = torch.full((cs.E,), 7, dtype=torch.int32, device=DEV)
+    offsets = torch.full((cs.E + 1,), 7, dtype=torch.int32, device=DEV)
+    z = torch.empty((0, cs.H), dtype=torch.bfloat16, device=DEV)
+    zl = torch.empty((0, cs.E), dtype=torch.float32, device=DEV)
+    w13 = torch.zeros((cs.E, 2 * cs.I, cs.H), dtype=torch.bfloat16, device=DEV)
+    w2 = torch.zeros((cs.E, cs.H, cs.I), dtype=torch.bfloat16, device=DEV)
+    rde.moe_forward(p, z, zl, None, None, w13, w2, None, None, None, None, z,
+                    dict(counts=counts, offsets=offsets), ws)
+    torch.cuda.synchronize()
+    assert counts.sum().item() == 0 and offsets.sum().item() == 0
+
+
+def test_forward_matches_separate_entry_points():
+    for key in ("decode_shared_small", "ragged_skew_capacity", "tiny_fp32"):
+        cs = _case(key)
+        _say("forward vs separate", key)
+        inp_dev = synth.make_inputs(cs, DEV)
+        out_f, meta, _ = _forward_gpu(cs, inp_dev)
+        p = problem(cs)
+        ws = workspace(p)
+        R = r_max(cs)
+        ids = torch.empty((cs.T, cs.k), dtype=torch.int32, device=DEV)
+        w = torch.empty((cs.T, cs.k), dtype=torch.float32, device=DEV)
+        rde.moe_route(p, inp_dev.logits, ids, w, ws)
+        counts = torch.empty(cs.E, dtype=torch.int32, device=DEV)
+        offsets = torch.empty(cs.E + 1, dtype=torch.int32, device=DEV)
+        row_src = torch.empty(max(R, 1), dtype=torch.int32, device=DEV)
+        route_dst = torch.empty((cs.T, cs.k), dtype=torch.int32, device=DEV)
+        x_disp = torch.empty((max(R, 1), cs.H), dtype=act_dtype(cs), device=DEV)
+        rde.moe_dispatch(p, inp_dev.x, ids, counts, offsets, row_src, route_dst, x_disp, ws)
+        y = torch.empty((max(R, 1), cs.H), dtype=act_dtype(cs), device=DEV)
+        rde.moe_expert_ffn(p, x_disp, offsets, inp_dev.w13, inp_dev.w2, inp_dev.s13, inp_dev.s2,
+                           y, ws)
+        ysh = None
+        if cs.n_shared:
+            ysh = torch.empty((cs.T, cs.H), dtype=torch.float32, device=DEV)
+            rde.moe_shared_ffn(p, inp_dev.x, inp_dev.w13_sh, inp_dev.w2_sh, ysh, ws)
+        out_s = torch.empty_like(out_f)
+        rde.moe_combine(p, y, route_dst, w, ysh, out_s, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, meta["ids"]) and torch.equal(w, meta["w"])
+        assert torch.equal(route_dst, meta["route_dst"]) and torch.equal(offsets, meta["offsets"])
+        ref = out_s.double().cpu().numpy()
+        assert_close(cs, out_f, ref, "fused vs separate")
