@@ -1,0 +1,238 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+A step is one moe_forward call (route -> count-first dispatch -> expert FFN
+-> combine) over one batch of synthetic, HBM-resident inputs.  The default
+workload is the prefill dispatch shape: T = 2048 tokens, hidden 2048, 128
+experts, top-8, capacity 2048, SwiGLU intermediate 1024, bf16 with float32
+accumulation, router logits N(0, 1).  The other token buckets (256, 8192)
+are timed as a short sweep.
+
+Printed: one JSON line with tokens/s (whole job), us per layer, the stage
+breakdown from HIP events recorded by the library on its stream inside the
+timed region, the roofline of the dominant kernel, and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+N_BANKS = 4                  # rotating x / logits banks
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_T2048")
+    ap.add_argument("--sweep", default="prefill_T256,prefill_T8192",
+                    help="comma-separated extra workloads timed briefly ('' = none)")
+    ap.add_argument("--cpu-tokens", type=int, default=128,
+                    help="tokens of the CPU oracle sample (0 = skip)")
+    return ap.parse_args()
+
+
+def stage_bytes_flops(cs, R, touched, ab, wb):
+    """Algorithmic bytes and flops of each stage for a batch with R kept
+    rows and `touched` non-empty experts."""
+    T, H, E, k, I = cs.T, cs.H, cs.E, cs.k, cs.I
+    Q = T * k
+    r_max = min(Q, E * cs.C)
+    n_w = 2 * I if cs.act == 0 else I
+    sc = 4 if wb == 1 else 0          # e4m3 per-row scales
+    st = {
+        "route": (T * E * 4 + Q * 8, 0),
+        "count": (Q * 4 + Q * 8 + E * 8, 0),
+        "scatter": (T * H * ab + R * H * ab + Q * 16 + r_max * 4, 0),
+        "gemm1": (touched * n_w * (H * wb + sc) + R * H * ab + R * I * ab, 2 * R * H * n_w),
+        "gemm2": (touched * H * (I * wb + sc) + R * I * ab + R * H * ab + R * 8, 2 * R * I * H),
+        "shared": (0, 0),
+        "combine": (R * H * ab + T * H * ab + Q * 4, 0),
+    }
+    if cs.n_shared:
+        Is, S = cs.I_shared, cs.n_shared
+        st["shared"] = (S * 3 * Is * H * 2 + T * H * ab + T * H * 4 + 2 * T * S * Is * ab,
+                        S * 2 * T * H * 3 * Is)
+    return st
+
+
+def run_workload(name, steps, warmup, with_events=True):
+    import torch
+    import routing_dispatch_expert_amd as rde
+    import synth
+
+    dev = "cuda:0"
+    cs = synth.case(name)
+    base = synth.make_inputs(cs, dev)
+    banks = []
+    for b in range(N_BANKS):
+        cb = synth.replace(cs, seed=cs.seed + 1000 * b)
+        banks.append((synth.make_x(cb, dev), synth.make_logits(cb, dev)))
+    p = rde.make_problem(cs.T, cs.H, cs.E, cs.k, cs.I, cs.C, cs.n_shared, cs.I_shared,
+                         act_dtype=cs.act_fmt, w_dtype=cs.w_fmt, act=cs.act)
+    n = rde.moe_workspace_bytes(p)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    rde.moe_workspace_init(ws)
+    adt = torch.float32 if cs.act_fmt == synth.FMT_F32 else torch.bfloat16
+    out = torch.empty((cs.T, cs.H), dtype=adt, device=dev)
+    offsets = torch.empty(cs.E + 1, dtype=torch.int32, device=dev)
+    n_ev = rde.MOE_N_STAGES
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    for row in evs:          # torch creates the HIP event on its first record
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        x, lg = banks[i % N_BANKS]
+        meta = dict(offsets=offsets)
+        if ev is not None:
+            meta["stage_events"] = ev
+        rde.moe_forward(p, x, lg, None, None, base.w13, base.w2, base.s13, base.s2,
+                        base.w13_sh, base.w2_sh, out, meta, ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, evs[i] if with_events else None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if rde.moe_error(ws) != 0:
+        raise RuntimeError("malformed routes reported on synthetic inputs")
+    stages = {}
+    if with_events:
+        for s in range(1, n_ev):
+            d = [evs[i][s - 1].elapsed_time(evs[i][s]) * 1e3 for i in range(steps)]  # us
+            stages[rde.STAGES[s]] = sum(d) / len(d)
+    # kept rows / touched experts of the last step's batch (outside the timed region)
+    off = offsets.cpu().tolist()
+    R = off[-1]
+    touched = sum(1 for e in range(cs.E) if off[e + 1] > off[e])
+    ab = 4 if cs.act_fmt == synth.FMT_F32 else 2
+    wb = {synth.FMT_F32: 4, synth.FMT_BF16: 2, synth.FMT_E4M3: 1}[cs.w_fmt]
+    return dict(cs=cs, wall=wall, stages=stages, R=R, touched=touched,
+                bf=stage_bytes_flops(cs, R, touched, ab, wb), base=base)
+
+
+def roofline_of(res, stage):
+    us = res["stages"][stage]
+    byts, flops = res["bf"][stage]
+    t_hbm = byts / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = flops / (BF16_PEAK_TFLOPS * 1e12)
+    if t_mfma > t_hbm:
+        ach = flops / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": stage, "us": round(us, 2), "alg_flops": flops, "alg_bytes": byts}
+    ach = byts / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": stage,
+            "us": round(us, 2), "alg_bytes": byts, "alg_flops": flops}
+
+
+def summary(res):
+    cs, st, bf = res["cs"], res["stages"], res["bf"]
+    disp_us = st["count"] + st["scatter"]
+    disp_b = bf["count"][0] + bf["scatter"][0]
+    g_us = st["gemm1"] + st["gemm2"]
+    g_fl = bf["gemm1"][1] + bf["gemm2"][1]
+    return {
+        "us_per_layer": round(sum(st.values()), 2),
+        "dispatch_GBps": round(disp_b / (disp_us * 1e-6) / 1e9, 1),
+        "gemm_mfma_pct": round(100 * g_fl / (g_us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 2),
+        "gemm_hbm_GBps": round((bf["gemm1"][0] + bf["gemm2"][0]) / (g_us * 1e-6) / 1e9, 1),
+        "kept_rows": res["R"], "experts_touched": res["touched"],
+        "stages_us": {k: round(v, 2) for k, v in st.items()},
+    }
+
+
+def cpu_baseline(res, n_tokens):
+    """The oracle as it stands, single-threaded, on the first n_tokens tokens
+    of the same workload (same weights, capacity and expert count)."""
+    import oracle
+    import synth
+
+    cs = res["cs"]
+    sub = synth.replace(cs, T=n_tokens)
+    base = res["base"]
+    x = oracle.from_torch(base.x[:n_tokens])
+    lg = oracle.from_torch(base.logits[:n_tokens])
+    w13 = oracle.from_torch(base.w13)
+    w2 = oracle.from_torch(base.w2)
+    conv = lambda t: None if t is None else oracle.from_torch(t)
+    r = oracle.forward(sub, x, lg, w13, w2, conv(base.s13), conv(base.s2), conv(base.w13_sh),
+                       conv(base.w2_sh))
+    sec = r["seconds"]
+    return {"value": round(n_tokens / sec, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_tokens} of {cs.T} tokens of {cs.name}: routing, count-first "
+                      f"dispatch, expert FFN and combine for them ({sec:.1f} s)",
+            "us_per_layer_extrapolated": round(sec / n_tokens * cs.T * 1e6, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              f"multi-GPU path: see the sharding design notes.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    print(f"[bench] workload {args.workload}: warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+    res = run_workload(args.workload, args.steps, args.warmup)
+    cs = res["cs"]
+    ms = res["wall"] / args.steps * 1e3
+    summ = summary(res)
+    dom = max((s for s in res["stages"]), key=lambda s: res["stages"][s])
+    line = {
+        "metric": "MoE layer tokens/s + us/layer; dispatch HBM GB/s, grouped-GEMM MFMA % of peak",
+        "value": round(cs.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cs.act_fmt == 1 else "f32",
+        "data": "synthetic",
+        "config": {"workload": cs.name, "T": cs.T, "H": cs.H, "E": cs.E, "k": cs.k, "I": cs.I,
+                   "C": cs.C, "act": "swiglu" if cs.act == 0 else "relu2",
+                   "weights": {0: "f32", 1: "bf16", 2: "e4m3"}[cs.w_fmt],
+                   "n_shared": cs.n_shared, "parallelism": "none (1 GPU)"},
+        **summ,
+        "roofline": roofline_of(res, dom),
+    }
+    print(f"[bench] {cs.name}: {ms*1e3:.1f} us/step, stages {summ['stages_us']}",
+          file=sys.stderr, flush=True)
+    if args.cpu_tokens > 0:
+        print(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens", file=sys.stderr,
+              flush=True)
+        line["cpu_baseline"] = cpu_baseline(res, args.cpu_tokens)
+    del res["base"]
+    sweep = {}
+    for name in [s for s in args.sweep.split(",") if s]:
+        print(f"[bench] sweep {name}", file=sys.stderr, flush=True)
+        r2 = run_workload(name, max(5, args.steps // 3), 3)
+        ms2 = r2["wall"] / max(5, args.steps // 3) * 1e3
+        sw = summary(r2)
+        sw["tokens_per_s"] = round(r2["cs"].T / (ms2 * 1e-3), 1)
+        sw["ms_per_step"] = round(ms2, 4)
+        d2 = max(r2["stages"], key=lambda s: r2["stages"][s])
+        sw["roofline"] = roofline_of(r2, d2)
+        sweep[name] = sw
+        del r2
+        torch.cuda.empty_cache()
+    if sweep:
+        line["sweep"] = sweep
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

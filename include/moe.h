@@ -108,8 +108,24 @@ typedef struct moe_problem {
     int32_t renormalize; /* 0: w = softmax over all E; 1: softmax over the k selected */
 } moe_problem;
 
+/* Stage boundaries of moe_forward, for moe_meta.stage_events. */
+#define MOE_STAGE_BEGIN 0    /* before the first kernel */
+#define MOE_STAGE_ROUTE 1    /* after the router (or the copy of preselected routes) */
+#define MOE_STAGE_COUNT 2    /* after the histogram / rank / scan kernel */
+#define MOE_STAGE_SCATTER 3  /* after the row scatter */
+#define MOE_STAGE_GEMM1 4    /* after the gate/up projection with its activation */
+#define MOE_STAGE_GEMM2 5    /* after the down projection (routing weights applied) */
+#define MOE_STAGE_SHARED 6   /* after the shared experts */
+#define MOE_STAGE_COMBINE 7  /* after the final sum to token order */
+#define MOE_N_STAGES 8
+
 /* Optional metadata outputs of moe_forward (any field may be NULL; a NULL
- * field is kept in the workspace instead).  Layouts as above. */
+ * field is kept in the workspace instead).  Layouts as above.
+ * stage_events: NULL, or MOE_N_STAGES hipEvent_t handles (entries may be
+ * NULL) that moe_forward records on `stream` at the stage boundaries above,
+ * so a caller can time each kernel with events on the stream it runs on.
+ * Stages that do no work record their event at the same point as the
+ * previous one. */
 typedef struct moe_meta {
     int32_t *ids;
     float *w;
@@ -117,6 +133,7 @@ typedef struct moe_meta {
     int32_t *offsets;
     int32_t *row_src;
     int32_t *route_dst;
+    void *const *stage_events;
 } moe_meta;
 
 /* Workspace size in bytes for problem `p` (the same for every entry point).

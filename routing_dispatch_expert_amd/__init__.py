@@ -31,8 +31,13 @@ class moe_problem(C.Structure):
                                          "act_dtype", "w_dtype", "act", "renormalize")]
 
 
+MOE_N_STAGES = 8
+STAGES = ("begin", "route", "count", "scatter", "gemm1", "gemm2", "shared", "combine")
+
+
 class moe_meta(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in ("ids", "w", "counts", "offsets", "row_src", "route_dst")]
+    _fields_ = [(n, C.c_void_p) for n in ("ids", "w", "counts", "offsets", "row_src", "route_dst",
+                                          "stage_events")]
 
 
 class MoeError(RuntimeError):
@@ -155,10 +160,17 @@ def moe_combine(p, y_disp, route_dst, w, y_shared, out, ws, stream=None):
 def moe_forward(p, x, logits, ids_in, w_in, w13, w2, s13, s2, w13_sh, w2_sh, out, meta, ws,
                 stream=None):
     """`meta` is None or a dict with any of ids, w, counts, offsets, row_src,
-    route_dst (device tensors receiving the metadata)."""
+    route_dst (device tensors receiving the metadata) and stage_events (a
+    list of MOE_N_STAGES torch.cuda.Event or None)."""
     m = None
+    keep = None
     if meta:
-        m = moe_meta(*[_p(meta.get(n)) for n, _ in moe_meta._fields_])
+        vals = [_p(meta.get(n)) for n, _ in moe_meta._fields_[:6]]
+        evs = meta.get("stage_events")
+        if evs is not None:
+            assert len(evs) == MOE_N_STAGES
+            keep = (C.c_void_p * MOE_N_STAGES)(*[None if e is None else e.cuda_event for e in evs])
+        m = moe_meta(*vals, C.cast(keep, C.c_void_p) if keep is not None else None)
     _check("moe_forward", lib().moe_forward(
         C.byref(p), _p(x), _p(logits), _p(ids_in), _p(w_in), _p(w13), _p(w2), _p(s13), _p(s2),
         _p(w13_sh), _p(w2_sh), _p(out), C.byref(m) if m is not None else None, _p(ws),

@@ -106,8 +106,10 @@ moe_status check_ws(const moe_problem& p, void* ws, size_t ws_bytes, Layout* L) 
 
 inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Persistent grid of the bf16 GEMM: one 512-thread workgroup per CU (its LDS
+// stages take most of the CU's 160 KB), a multiple of 8 (XCD count).
 int gemm_grid(int64_t tiles_upper) {
-    int g = device_cu_count() * 2;
+    int g = device_cu_count();
     g = (g + 7) / 8 * 8;
     if (tiles_upper < g) g = (int)((tiles_upper + 7) / 8 * 8);
     return g > 8 ? g : 8;
@@ -140,7 +142,7 @@ hipError_t run_gemm1(const moe_problem& p, const void* x_disp, const int32_t* of
         a.n_tiles = p.act == MOE_SWIGLU ? p.I / 32 : p.I / 64;
         return launch_gemm_f32(a, gemm_grid((R / kGemmF32BM + p.E) * a.n_tiles), s);
     }
-    a.n_tiles = p.act == MOE_SWIGLU ? p.I / 64 : p.I / 128;
+    a.n_tiles = p.act == MOE_SWIGLU ? p.I / 128 : (p.I + 255) / 256;
     return launch_gemm_bf16(a, p.w_dtype, gemm_grid((R / kGemmBM + p.E) * a.n_tiles), s);
 }
 
@@ -172,7 +174,7 @@ hipError_t run_gemm2(const moe_problem& p, const void* h, const int32_t* offsets
         a.n_tiles = p.H / 64;
         return launch_gemm_f32(a, gemm_grid((R / kGemmF32BM + p.E) * a.n_tiles), s);
     }
-    a.n_tiles = p.H / 128;
+    a.n_tiles = (p.H + 255) / 256;
     return launch_gemm_bf16(a, p.w_dtype, gemm_grid((R / kGemmBM + p.E) * a.n_tiles), s);
 }
 
@@ -205,7 +207,7 @@ hipError_t run_shared(const moe_problem& p, const void* x, const void* w13_sh, c
         a.n_tiles = Is / 32;
         e = launch_gemm_f32(a, gemm_grid(mt * S * a.n_tiles), s);
     } else {
-        a.n_tiles = Is / 64;
+        a.n_tiles = Is / 128;
         e = launch_gemm_bf16(a, wdt, gemm_grid(mt * S * a.n_tiles), s);
     }
     if (e != hipSuccess) return e;
@@ -227,8 +229,13 @@ hipError_t run_shared(const moe_problem& p, const void* x, const void* w13_sh, c
         b.n_tiles = p.H / 64;
         return launch_gemm_f32(b, gemm_grid(mt * b.n_tiles), s);
     }
-    b.n_tiles = p.H / 128;
+    b.n_tiles = (p.H + 255) / 256;
     return launch_gemm_bf16(b, wdt, gemm_grid(mt * b.n_tiles), s);
+}
+
+inline hipError_t mark(const moe_meta& m, int stage, hipStream_t s) {
+    if (!m.stage_events || !m.stage_events[stage]) return hipSuccess;
+    return hipEventRecord((hipEvent_t)m.stage_events[stage], s);
 }
 
 moe_status check_ptrs16(std::initializer_list<const void*> ps) {
@@ -371,38 +378,46 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
     int32_t* route_dst = m.route_dst ? m.route_dst : at<int32_t>(ws, L.route_dst);
     hipStream_t s = (hipStream_t)stream;
     const int64_t Q = (int64_t)P.T * P.k;
-    hipError_t e = hipSuccess;
-    if (pre) {
+    hipError_t e = mark(m, MOE_STAGE_BEGIN, s);
+    if (e == hipSuccess && pre) {
         // preselected routes: copy into the metadata outputs when they differ
         if (ids != ids_in && Q) e = hipMemcpyAsync(ids, ids_in, sizeof(int32_t) * Q, hipMemcpyDeviceToDevice, s);
         if (e == hipSuccess && w != w_in && Q)
             e = hipMemcpyAsync(w, w_in, sizeof(float) * Q, hipMemcpyDeviceToDevice, s);
-    } else if (P.T > 0) {
+    } else if (e == hipSuccess && P.T > 0) {
         e = launch_route(logits, P.T, P.E, P.k, P.renormalize, ids, w, s);
     }
+    if (e == hipSuccess) e = mark(m, MOE_STAGE_ROUTE, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     void* x_disp = at<void>(ws, L.x_disp);
     int32_t* mt = at<int32_t>(ws, L.mt_off);
     e = launch_count_rank(ids, P.T, P.k, P.E, P.C, gemm_bm(P), at<int32_t>(ws, L.rexp),
                           at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), counts, offsets, mt,
                           at<int32_t>(ws, L.ctrl), s);
+    if (e == hipSuccess) e = mark(m, MOE_STAGE_COUNT, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    if (P.T == 0) return MOE_OK;
-    e = launch_scatter(x, P.T, P.H, P.k, P.E, P.C, act_bytes(P), r_max_of(P), at<int32_t>(ws, L.rexp),
-                       at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), offsets, route_dst, row_src,
-                       x_disp, s);
+    if (P.T > 0)
+        e = launch_scatter(x, P.T, P.H, P.k, P.E, P.C, act_bytes(P), r_max_of(P), at<int32_t>(ws, L.rexp),
+                           at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), offsets, route_dst,
+                           row_src, x_disp, s);
+    if (e == hipSuccess) e = mark(m, MOE_STAGE_SCATTER, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     void* h = at<void>(ws, L.h);
     void* ybuf = at<void>(ws, L.ybuf);
     float* y_sh = P.n_shared ? at<float>(ws, L.y_shared) : nullptr;
-    if (r_max_of(P) > 0) {
-        if (run_gemm1(P, x_disp, offsets, mt, w13, s13, h, s) != hipSuccess) return MOE_ERR_HIP;
-        if (run_gemm2(P, h, offsets, mt, w2, s2, EPI_COMBINE, ybuf, w, row_src, s) != hipSuccess)
-            return MOE_ERR_HIP;
-    }
-    if (P.n_shared && run_shared(P, x, w13_sh, w2_sh, at<void>(ws, L.h_sh), y_sh, s) != hipSuccess)
-        return MOE_ERR_HIP;
-    return hip_status(launch_combine(ybuf, 0, route_dst, nullptr, y_sh, out, P.T, P.k, P.H, P.act_dtype, s));
+    const bool work = P.T > 0 && r_max_of(P) > 0;
+    if (work) e = run_gemm1(P, x_disp, offsets, mt, w13, s13, h, s);
+    if (e == hipSuccess) e = mark(m, MOE_STAGE_GEMM1, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (work) e = run_gemm2(P, h, offsets, mt, w2, s2, EPI_COMBINE, ybuf, w, row_src, s);
+    if (e == hipSuccess) e = mark(m, MOE_STAGE_GEMM2, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (P.T > 0 && P.n_shared) e = run_shared(P, x, w13_sh, w2_sh, at<void>(ws, L.h_sh), y_sh, s);
+    if (e == hipSuccess) e = mark(m, MOE_STAGE_SHARED, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (P.T > 0) e = launch_combine(ybuf, 0, route_dst, nullptr, y_sh, out, P.T, P.k, P.H, P.act_dtype, s);
+    if (e == hipSuccess) e = mark(m, MOE_STAGE_COMBINE, s);
+    return hip_status(e);
 }
 
 moe_status moe_error(void* ws, size_t ws_bytes, void* stream, int32_t* n_invalid_routes) {

@@ -84,7 +84,7 @@ struct GemmArgs {
     int I;                      // EPI_SWIGLU: up rows start at I in B
 };
 
-constexpr int kGemmBM = 128;   // rows per m-tile of the bf16 MFMA kernel
+constexpr int kGemmBM = 256;   // rows per m-tile of the bf16 MFMA kernel
 constexpr int kGemmF32BM = 64; // rows per m-tile of the f32 kernel
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int w_dtype, int grid, hipStream_t s);

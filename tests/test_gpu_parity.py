@@ -28,6 +28,9 @@ SMALL = {
     "fp8_small": ("skewed_fp8", dict(T=300, H=256, E=8, I=256, C=96)),
     "k1_e1": ("prefill_T256", dict(T=130, H=128, E=1, k=1, I=128, C=130)),
     "fp32_relu2_renorm": ("tiny_fp32", dict(act=synth.ACT_RELU2, renormalize=1, T=100, C=40)),
+    # hidden / intermediate not multiples of the 256-column tile
+    "ragged_n_relu2": ("relu2_distinct_R8", dict(H=384, I=384)),
+    "ragged_n_swiglu": ("prefill_T256", dict(T=300, H=384, E=4, k=2, I=384, C=300)),
 }
 # Full-size workloads.
 FULL = ["tiny_fp32", "prefill_T256", "prefill_T2048", "prefill_T8192", "decode_T1", "decode_T8",
