@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--workload", default="prefill_T2048")
     ap.add_argument("--sweep", default="prefill_T256,prefill_T8192",
                     help="comma-separated extra workloads timed briefly ('' = none)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one device copy of this size first (counter calibration)")
     ap.add_argument("--cpu-tokens", type=int, default=128,
                     help="tokens of the CPU oracle sample (0 = skip)")
     return ap.parse_args()
@@ -186,6 +188,14 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: {n} bytes", file=sys.stderr, flush=True)
+        del src, dst
     print(f"[bench] workload {args.workload}: warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
     res = run_workload(args.workload, args.steps, args.warmup)
