@@ -32,7 +32,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_T2048")
-    ap.add_argument("--sweep", default="prefill_T256,prefill_T8192",
+    ap.add_argument("--sweep", default="prefill_T256,prefill_T8192,decode_T1,decode_T32,"
+                    "relu2_distinct_R16,relu2_shared_R1",
                     help="comma-separated extra workloads timed briefly ('' = none)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
@@ -103,11 +104,22 @@ def run_workload(name, steps, warmup, with_events=True):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    # timed region 1: plain steps (the throughput figure)
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, evs[i] if with_events else None)
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # timed region 2: the same steps with the library recording an event at
+    # every stage boundary on its stream (per-kernel durations; each event
+    # adds a few microseconds, so this region is not the throughput figure)
+    wall_ev = None
+    if with_events:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        wall_ev = time.perf_counter() - t0
     if rde.moe_error(ws) != 0:
         raise RuntimeError("malformed routes reported on synthetic inputs")
     stages = {}
@@ -121,7 +133,7 @@ def run_workload(name, steps, warmup, with_events=True):
     touched = sum(1 for e in range(cs.E) if off[e + 1] > off[e])
     ab = 4 if cs.act_fmt == synth.FMT_F32 else 2
     wb = {synth.FMT_F32: 4, synth.FMT_BF16: 2, synth.FMT_E4M3: 1}[cs.w_fmt]
-    return dict(cs=cs, wall=wall, stages=stages, R=R, touched=touched,
+    return dict(cs=cs, steps=steps, wall=wall, wall_ev=wall_ev, stages=stages, R=R, touched=touched,
                 bf=stage_bytes_flops(cs, R, touched, ab, wb), base=base)
 
 
@@ -148,12 +160,15 @@ def summary(res):
     g_us = st["gemm1"] + st["gemm2"]
     g_fl = bf["gemm1"][1] + bf["gemm2"][1]
     return {
-        "us_per_layer": round(sum(st.values()), 2),
+        "us_per_layer": round(res["wall"] / res["steps"] * 1e6, 2),
+        "sum_of_stage_us": round(sum(st.values()), 2),
         "dispatch_GBps": round(disp_b / (disp_us * 1e-6) / 1e9, 1),
         "gemm_mfma_pct": round(100 * g_fl / (g_us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 2),
         "gemm_hbm_GBps": round((bf["gemm1"][0] + bf["gemm2"][0]) / (g_us * 1e-6) / 1e9, 1),
         "kept_rows": res["R"], "experts_touched": res["touched"],
         "stages_us": {k: round(v, 2) for k, v in st.items()},
+        "ms_per_step_with_stage_events": round(res["wall_ev"] / res["steps"] * 1e3, 4)
+        if res.get("wall_ev") else None,
     }
 
 

@@ -31,12 +31,14 @@
 // e4m3 weights are widened to bf16 exactly while being staged into LDS (the
 // hardware converts OCP e4m3 to float32; every e4m3 value is a bf16 value)
 // and the per-row scale multiplies the float32 accumulator.
+#include <type_traits>
+
 #include "common.h"
 
 namespace rde {
 namespace {
 
-constexpr int BM = kGemmBM, BN = 256, BK = 64, LDK = BK + 8;
+constexpr int BM = kGemmBM, BN = 256, BK = 32;
 constexpr int kThreads = 512;   // 8 waves: 2 (M) x 4 (N)
 constexpr int kMaxGroupsLds = 1024;
 
@@ -68,25 +70,96 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
     return make_uint2(pack_bf16x2(lo.x, lo.y), pack_bf16x2(hi.x, hi.y));
 }
 
-// 16 e4m3 codes -> 16 bf16 written to LDS (two 16-byte stores).
-__device__ __forceinline__ void stage_e4m3(__bf16* dst, uint4 v) {
-    const uint2 p0 = e4m3x4_to_bf16x4(v.x), p1 = e4m3x4_to_bf16x4(v.y);
-    const uint2 p2 = e4m3x4_to_bf16x4(v.z), p3 = e4m3x4_to_bf16x4(v.w);
-    *(uint4*)dst = make_uint4(p0.x, p0.y, p1.x, p1.y);
-    *(uint4*)(dst + 8) = make_uint4(p2.x, p2.y, p3.x, p3.y);
+// ---- bf16 MFMA kernel --------------------------------------------------------
+// Block tile BM x BN x BK = 256 x 256 x 32, 8 waves, a ring of kStages LDS
+// stages filled by direct global -> LDS loads (global_load_lds_dwordx4: lane l
+// of a wave writes the 16 bytes it loads to LDS base + 16*l).  kStages - 1
+// k-tiles are in flight while one is multiplied; one barrier per k-tile.
+//
+// Each tile walks K starting at a rotated k-tile (see `rot` below).
+//
+// LDS rows of a bf16 stage are 64 bytes (4 chunks of 16 B).  Chunk c of row r
+// is stored at chunk slot c ^ swz(r), swz(r) = (r1 ^ r3) | r2 << 1 (r_i = bit i
+// of r): 8 consecutive rows reading one logical chunk hit 8 distinct 16-byte
+// slots modulo 128 bytes, and 16 consecutive rows hit 16 distinct slots
+// modulo 256 bytes, so the fragment reads are free of bank conflicts whether
+// the LDS serves 8 or 16 lanes of a ds_read_b128 per clock.  A DMA block of one
+// wave instruction is 16 rows x 64 B; lane l fills row l/4, slot l%4 and so
+// loads the row's logical chunk (l%4) ^ swz(row).
+//
+// e4m3 weights stay e4m3 in LDS (32-byte rows, two 16-byte halves swapped on
+// bit 2 of the row) and are widened exactly to bf16 when a fragment is read.
+constexpr int kStages = 4;
+constexpr int A_STAGE = BM * BK * 2;          // bytes of one A stage (16 KB)
+constexpr int B_STAGE_BF16 = BN * BK * 2;     // 16 KB
+constexpr int B_STAGE_E4M3 = BN * BK;         // 8 KB
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 1 | (((r >> 2) & 1) << 1); }
+
+// LDS byte address of a __shared__ object (32-bit, as the hardware sees it).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
 }
 
-// Block tile BM x BN x BK = 256 x 256 x 64, 8 waves.  Wave (wm, wn) owns
-// the 32-row blocks wm, wm+2, wm+4, wm+6 (interleaved, so a half-filled
-// tile keeps both M-waves busy) and B rows wn*64 .. wn*64+63.  The MFMA is
-// issued as B x A^T so each lane ends with 4 consecutive output columns of
-// one row (vector stores in the epilogue): for acc register r of a 32x32
-// block, row = lane % 32, column = 8*(r/4) + 4*(lane/32) + r%4.
-// LDS: two stages of A and B tiles, rows padded to 72 elements.
+// One direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at LDS address `lds` + 16*l; `lds` must be wave-uniform.
+// Written as inline assembly so that the compiler's wait-count pass, which
+// cannot tell the ring's stages apart, does not drain every in-flight load
+// before each LDS read: the k-loop orders the ring itself with an explicit
+// vmcnt wait and a barrier.  M0 (the LDS base register of the instruction)
+// is saved and restored around the load.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(lds)
+        : "memory");
+}
+
+// Wait until at most n of this thread's vector-memory operations are
+// outstanding (n known at compile time per case), then workgroup barrier.
+// No memory fence: LDS written by global_load_lds is complete once the
+// issuing thread's vmcnt has dropped past it.
+template <int L>
+__device__ __forceinline__ void wait_tiles_barrier(int tiles_after) {
+    if (tiles_after >= 2) {
+        if (L == 4) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else if (tiles_after == 1) {
+        if (L == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+}
+
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 8 e4m3 codes (two dwords) -> bf16x8, exact.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint2 v) {
+    const uint2 lo = e4m3x4_to_bf16x4(v.x), hi = e4m3x4_to_bf16x4(v.y);
+    const uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// Wave tile 128 x 64: wave (wm, wn) owns the 32-row blocks wm, wm+2, wm+4,
+// wm+6 (interleaved, so a half-filled tile keeps both M-waves busy) and B
+// rows wn*64 .. wn*64+63.  The MFMA is issued as B x A^T so each lane ends
+// with 4 consecutive output columns of one row: for acc register r of a
+// 32x32 block, row = lane % 32, column = 8*(r/4) + 4*(lane/32) + r%4.
 template <int EPI, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) __bf16 sA[2][BM * LDK];
-    __shared__ __attribute__((aligned(16))) __bf16 sB[2][BN * LDK];
+    constexpr int B_STAGE = FP8 ? B_STAGE_E4M3 : B_STAGE_BF16;
+    constexpr int L = FP8 ? 3 : 4;  // DMA instructions per thread per k-tile
+    __shared__ __attribute__((aligned(1024))) unsigned char sA[kStages][A_STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char sB[kStages][B_STAGE];
     __shared__ int32_t s_mt[kMaxGroupsLds + 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -111,28 +184,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     const int G = gridDim.x;
     const int vid = ((G & 7) == 0) ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
 
-    const __bf16* A = (const __bf16*)a.A;
+    const char* Ab = (const char*)a.A;
     const char* Bb = (const char*)a.B;
     const int nk = a.K / BK;
-    // global -> register staging plan: A 256 rows x 8 chunks of 16 B (4 per
-    // thread); B bf16 likewise, B e4m3 256 rows x 4 chunks (2 per thread)
-    const int ac = tid & 7, ar = tid >> 3;          // A: rows ar + 64*i
-    const int bc = FP8 ? (tid & 3) : (tid & 7);
-    const int br = FP8 ? (tid >> 2) : (tid >> 3);   // B: rows br + (FP8 ? 128 : 64)*i
-    constexpr int BRS = FP8 ? 128 : 64;
 
-    for (int64_t L = vid; L < total; L += G) {
+    // DMA plan.  A: wave w fills rows w*32 + 16*b + lane/4 (b = 0, 1).
+    const int dr = lane >> 2, ds = lane & 3;
+    // bf16 B: same shape as A.  e4m3 B: wave w fills rows w*32 + lane/2,
+    // 16-byte half lane%2 (one instruction per k-tile).
+
+    for (int64_t Lt = vid; Lt < total; Lt += G) {
         int g, cnt, ml, nt;
         if (uniform) {
-            g = (int)(L / ((int64_t)tiles_per_group * ntl));
-            const int loc = (int)(L - (int64_t)g * tiles_per_group * ntl);
+            g = (int)(Lt / ((int64_t)tiles_per_group * ntl));
+            const int loc = (int)(Lt - (int64_t)g * tiles_per_group * ntl);
             cnt = tiles_per_group;
             nt = loc / cnt;
             ml = loc - nt * cnt;
         } else {
-            g = find_group(s_mt, a.n_groups, L, ntl);
+            g = find_group(s_mt, a.n_groups, Lt, ntl);
             cnt = s_mt[g + 1] - s_mt[g];
-            const int loc = (int)(L - (int64_t)s_mt[g] * ntl);
+            const int loc = (int)(Lt - (int64_t)s_mt[g] * ntl);
             nt = loc / cnt;
             ml = loc - nt * cnt;
         }
@@ -145,12 +217,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
             a_row0 = e0 + ml * BM;
             rows = min(BM, e1 - a_row0);
         }
-
-        const __bf16* ap0 = A + (int64_t)(a_row0 + min(ar, rows - 1)) * a.lda + ac * 8;
-        const __bf16* ap1 = A + (int64_t)(a_row0 + min(ar + 64, rows - 1)) * a.lda + ac * 8;
-        const __bf16* ap2 = A + (int64_t)(a_row0 + min(ar + 128, rows - 1)) * a.lda + ac * 8;
-        const __bf16* ap3 = A + (int64_t)(a_row0 + min(ar + 192, rows - 1)) * a.lda + ac * 8;
-        // byte offsets of this thread's B rows (bf16: 4 rows, e4m3: 2 rows)
         auto brow_of = [&](int r) {
             if (EPI == EPI_SWIGLU) {
                 const int w2 = r >> 6, rr = r & 63;
@@ -158,12 +224,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
             }
             return min(nt * BN + r, a.N_w - 1);   // rows past N (ragged last tile): clamped
         };
+        // per-thread global byte offsets (k = 0) of its DMA sources
+        const int ra0 = wave * 32 + dr, ra1 = ra0 + 16;
+        const int64_t ga0 = (int64_t)(a_row0 + min(ra0, rows - 1)) * a.lda * 2 + ((ds ^ swz(ra0)) * 16);
+        const int64_t ga1 = (int64_t)(a_row0 + min(ra1, rows - 1)) * a.lda * 2 + ((ds ^ swz(ra1)) * 16);
         const int64_t gbase = (int64_t)g * a.b_group_stride;
-        const int esz = FP8 ? 1 : 2;
-        const int64_t boff0 = (gbase + (int64_t)brow_of(br) * a.k_seg) * esz + bc * 16;
-        const int64_t boff1 = (gbase + (int64_t)brow_of(br + BRS) * a.k_seg) * esz + bc * 16;
-        const int64_t boff2 = FP8 ? 0 : (gbase + (int64_t)brow_of(br + 2 * BRS) * a.k_seg) * esz + bc * 16;
-        const int64_t boff3 = FP8 ? 0 : (gbase + (int64_t)brow_of(br + 3 * BRS) * a.k_seg) * esz + bc * 16;
+        int64_t gb0, gb1 = 0;
+        if (FP8) {
+            const int rb = wave * 32 + (lane >> 1), hb = lane & 1;
+            gb0 = (gbase + (int64_t)brow_of(rb) * a.k_seg) + ((hb ^ ((rb >> 2) & 1)) * 16);
+        } else {
+            gb0 = (gbase + (int64_t)brow_of(ra0) * a.k_seg) * 2 + ((ds ^ swz(ra0)) * 16);
+            gb1 = (gbase + (int64_t)brow_of(ra1) * a.k_seg) * 2 + ((ds ^ swz(ra1)) * 16);
+        }
+        // wave-uniform LDS bases of this wave's DMA blocks in stage 0
+        const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(sA[0]) + wave * 2048);
+        const uint32_t lb0 = __builtin_amdgcn_readfirstlane(lds_addr(sB[0]) + wave * (FP8 ? 1024 : 2048));
+        // K order: the tile starts at k-tile `rot` and wraps.  Tiles running at
+        // the same time then read different column offsets of their rows, so
+        // rows with a power-of-two stride (weights and activations alike) do
+        // not all land on the same memory channels.  rot depends only on the
+        // expert and the n-tile, so a row's summation order never depends on
+        // the other tokens of the batch.
+        const int rot = (g * 7 + nt * 13) % nk;
+        auto issue = [&](int kt) {
+            const int slot = kt % kStages;
+            int kr = kt + rot;
+            if (kr >= nk) kr -= nk;
+            const int k0 = kr * BK;
+            const int seg = k0 / a.k_seg;
+            const int64_t bo = (int64_t)seg * a.b_seg_stride + (k0 - seg * a.k_seg);
+            const uint32_t la = la0 + slot * A_STAGE, lb = lb0 + slot * B_STAGE;
+            dma16(Ab + ga0 + (int64_t)k0 * 2, la);
+            dma16(Ab + ga1 + (int64_t)k0 * 2, la + 1024);
+            if (FP8) {
+                dma16(Bb + gb0 + bo, lb);
+            } else {
+                dma16(Bb + gb0 + bo * 2, lb);
+                dma16(Bb + gb1 + bo * 2, lb + 1024);
+            }
+        };
 
         f32x16 acc[4][2];
 #pragma unroll
@@ -172,83 +272,70 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-        // waves whose 64 B rows lie past N (ragged last n-tile) do no work
+        // active row blocks of this wave: wm + 2*mb is active iff 32*(wm + 2*mb) < rows,
+        // i.e. mb < n_act (a prefix); waves whose 64 B rows lie past N (ragged last
+        // n-tile) have none.  Wave-uniform, kept in a scalar register.
         const bool col_ok = EPI == EPI_SWIGLU || nt * BN + wn * 64 < a.N_w;
-        bool act[4];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) act[mb] = col_ok && 32 * (wm + 2 * mb) < rows;
+        const int n_act = __builtin_amdgcn_readfirstlane(
+            col_ok ? max(0, min(4, (rows - 32 * wm + 63) / 64)) : 0);
 
-        uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-#define RDE_LOAD(kt)                                                                     \
-    do {                                                                                 \
-        const int k0_ = (kt) * BK;                                                       \
-        ra0 = *(const uint4*)(ap0 + k0_);                                                \
-        ra1 = *(const uint4*)(ap1 + k0_);                                                \
-        ra2 = *(const uint4*)(ap2 + k0_);                                                \
-        ra3 = *(const uint4*)(ap3 + k0_);                                                \
-        const int seg_ = k0_ / a.k_seg;                                                  \
-        const int64_t so_ = ((int64_t)seg_ * a.b_seg_stride + (k0_ - seg_ * a.k_seg)) *  \
-                            (FP8 ? 1 : 2);                                               \
-        rb0 = *(const uint4*)(Bb + boff0 + so_);                                         \
-        rb1 = *(const uint4*)(Bb + boff1 + so_);                                         \
-        if (!FP8) {                                                                      \
-            rb2 = *(const uint4*)(Bb + boff2 + so_);                                     \
-            rb3 = *(const uint4*)(Bb + boff3 + so_);                                     \
-        }                                                                                \
-    } while (0)
-#define RDE_STORE(buf)                                                                   \
-    do {                                                                                 \
-        __bf16* sa_ = sA[buf];                                                           \
-        *(uint4*)&sa_[(ar)*LDK + ac * 8] = ra0;                                          \
-        *(uint4*)&sa_[(ar + 64) * LDK + ac * 8] = ra1;                                   \
-        *(uint4*)&sa_[(ar + 128) * LDK + ac * 8] = ra2;                                  \
-        *(uint4*)&sa_[(ar + 192) * LDK + ac * 8] = ra3;                                  \
-        __bf16* sb_ = sB[buf];                                                           \
-        if (FP8) {                                                                       \
-            stage_e4m3(sb_ + br * LDK + bc * 16, rb0);                                   \
-            stage_e4m3(sb_ + (br + BRS) * LDK + bc * 16, rb1);                           \
-        } else {                                                                         \
-            *(uint4*)&sb_[br * LDK + bc * 8] = rb0;                                      \
-            *(uint4*)&sb_[(br + BRS) * LDK + bc * 8] = rb1;                              \
-            *(uint4*)&sb_[(br + 2 * BRS) * LDK + bc * 8] = rb2;                          \
-            *(uint4*)&sb_[(br + 3 * BRS) * LDK + bc * 8] = rb3;                          \
-        }                                                                                \
-    } while (0)
+        barrier_lds();  // the previous tile's last stage is no longer read
+#pragma unroll
+        for (int st = 0; st < kStages - 1; ++st)
+            if (st < nk) issue(st);
 
-        RDE_LOAD(0);
-        RDE_STORE(0);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < nk) RDE_LOAD(kt + 1);
-            const __bf16* sa = sA[cur];
-            const __bf16* sb = sB[cur];
+        const int rA = lane & 31, half = lane >> 5;
+        // the pipelined k-loop, specialised on the number NA of active row blocks
+        auto kloop = [&](auto na_c) {
+            constexpr int NA = decltype(na_c)::value;
+            for (int kt = 0; kt < nk; ++kt) {
+                wait_tiles_barrier<L>(min(kStages - 2, nk - 1 - kt));
+                if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
+                if (NA == 0) continue;
+                const unsigned char* sa = sA[kt % kStages];
+                const unsigned char* sb = sB[kt % kStages];
 #pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                const int kof = ks * 16 + (lane >> 5) * 8;
-                const bf16x8 b0 = *(const bf16x8*)&sb[(wn * 64 + (lane & 31)) * LDK + kof];
-                const bf16x8 b1 = *(const bf16x8*)&sb[(wn * 64 + 32 + (lane & 31)) * LDK + kof];
+                for (int ks = 0; ks < BK / 16; ++ks) {
+                    const int c = ks * 2 + half;  // logical 16-byte chunk of this lane
+                    bf16x8 b0, b1, av[NA > 0 ? NA : 1];
+                    const int r0 = wn * 64 + rA, r1 = r0 + 32;
+                    if (FP8) {
+                        // piece c (8 bytes) of a 32-byte row; halves swapped on row bit 2
+                        const int p0 = ((c >> 1) ^ ((r0 >> 2) & 1)) * 16 + (c & 1) * 8;
+                        const int p1 = ((c >> 1) ^ ((r1 >> 2) & 1)) * 16 + (c & 1) * 8;
+                        b0 = e4m3x8_to_bf16x8(*(const uint2*)(sb + r0 * 32 + p0));
+                        b1 = e4m3x8_to_bf16x8(*(const uint2*)(sb + r1 * 32 + p1));
+                    } else {
+                        b0 = *(const bf16x8*)(sb + r0 * 64 + ((c ^ swz(r0)) * 16));
+                        b1 = *(const bf16x8*)(sb + r1 * 64 + ((c ^ swz(r1)) * 16));
+                    }
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    if (!act[mb]) continue;
-                    const bf16x8 av =
-                        *(const bf16x8*)&sa[((wm + 2 * mb) * 32 + (lane & 31)) * LDK + kof];
-                    acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, av, acc[mb][0], 0, 0, 0);
-                    acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, av, acc[mb][1], 0, 0, 0);
+                    for (int mb = 0; mb < NA; ++mb) {
+                        const int ra = (wm + 2 * mb) * 32 + rA;
+                        av[mb] = *(const bf16x8*)(sa + ra * 64 + ((c ^ swz(ra)) * 16));
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < NA; ++mb) {
+                        acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, av[mb], acc[mb][0], 0, 0, 0);
+                        acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, av[mb], acc[mb][1], 0, 0, 0);
+                    }
                 }
             }
-            if (kt + 1 < nk) RDE_STORE(cur ^ 1);
-            __syncthreads();
+        };
+        switch (n_act) {
+            case 4: kloop(std::integral_constant<int, 4>{}); break;
+            case 3: kloop(std::integral_constant<int, 3>{}); break;
+            case 2: kloop(std::integral_constant<int, 2>{}); break;
+            case 1: kloop(std::integral_constant<int, 1>{}); break;
+            default: kloop(std::integral_constant<int, 0>{}); break;
         }
-#undef RDE_LOAD
-#undef RDE_STORE
 
         // ---- epilogue: lane owns row (lane % 32) of each active row block and
         // columns 8*i + 4*(lane/32) + 0..3 of each 32-column block ----
         const int c4 = 4 * (lane >> 5);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            if (!act[mb]) continue;
+            if (mb >= n_act) continue;
             const int row = (wm + 2 * mb) * 32 + (lane & 31);
             if (row >= rows) continue;
             const int64_t orow = (int64_t)a_row0 + row;
