@@ -6,8 +6,10 @@
 // moe_error.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <climits>
+#include <cstdlib>
 #include <cstring>
 
 #include "common.h"
@@ -238,6 +240,142 @@ inline hipError_t mark(const moe_meta& m, int stage, hipStream_t s) {
     return hipEventRecord((hipEvent_t)m.stage_events[stage], s);
 }
 
+// ---- decode-shaped batches ---------------------------------------------------
+// Batches with few rows per expert run the expert GEMMs as slot-indexed
+// units (decode.hip): every touched expert's weights stream once over all
+// wavefronts and activation rows are read in place.  The switch point is an
+// average of kDecodeRowsPerExpert routes per expert (PR 33963 switches its
+// kernels on the route count, at 128 routes for 240 experts); the
+// environment variable MOE_DECODE_ROWS_PER_EXPERT overrides it (read once).
+constexpr int kDecodeRowsPerExpert = 12;
+
+int decode_rows_per_expert() {
+    static const int v = [] {
+        const char* e = std::getenv("MOE_DECODE_ROWS_PER_EXPERT");
+        return e ? std::atoi(e) : kDecodeRowsPerExpert;
+    }();
+    return v;
+}
+
+bool decode_mode(const moe_problem& p) {
+    return p.act_dtype == MOE_BF16 && (int64_t)p.T * p.k <= (int64_t)decode_rows_per_expert() * p.E;
+}
+
+int decode_grid() { return device_cu_count(); }  // 4 wavefronts x 32 KB LDS ring per CU
+
+DecodeSeg routed_seg1(const moe_problem& p, const void* A, int gather, const int32_t* offsets,
+                      const void* w13, const float* s13, void* h) {
+    DecodeSeg s = {};
+    s.A = A;
+    s.lda = p.H;
+    s.gather = gather;
+    s.offsets = offsets;
+    s.B = w13;
+    s.N_w = p.act == MOE_SWIGLU ? 2 * p.I : p.I;
+    s.b_group_stride = (int64_t)s.N_w * p.H;
+    s.k_seg = p.H;
+    s.bscale = s13;
+    s.K = p.H;
+    s.I = p.I;
+    s.epi = p.act == MOE_SWIGLU ? EPI_SWIGLU : EPI_RELU2;
+    s.out = h;
+    s.ldo = p.I;
+    s.n_groups = p.E;
+    s.blocks = p.act == MOE_SWIGLU ? p.I / 16 : p.I / 32;
+    return s;
+}
+
+DecodeSeg routed_seg2(const moe_problem& p, const void* h, const int32_t* offsets, const void* w2,
+                      const float* s2, int epi, void* out) {
+    DecodeSeg s = {};
+    s.A = h;
+    s.lda = p.I;
+    s.offsets = offsets;
+    s.B = w2;
+    s.N_w = p.H;
+    s.b_group_stride = (int64_t)p.H * p.I;
+    s.k_seg = p.I;
+    s.bscale = s2;
+    s.K = p.I;
+    s.epi = epi;
+    s.out = out;
+    s.ldo = p.H;
+    s.n_groups = p.E;
+    s.blocks = (p.H + 31) / 32;
+    return s;
+}
+
+DecodeSeg shared_seg1(const moe_problem& p, const void* x, const void* w13_sh, void* h_sh) {
+    const int Is = p.I_shared;
+    DecodeSeg s = {};
+    s.A = x;
+    s.lda = p.H;
+    s.uniform_rows = p.T;
+    s.B = w13_sh;
+    s.N_w = 2 * Is;
+    s.b_group_stride = (int64_t)2 * Is * p.H;
+    s.k_seg = p.H;
+    s.K = p.H;
+    s.I = Is;
+    s.epi = EPI_SWIGLU;
+    s.out = h_sh;
+    s.ldo = (int64_t)p.n_shared * Is;
+    s.out_col_per_group = Is;
+    s.n_groups = p.n_shared;
+    s.blocks = Is / 16;
+    return s;
+}
+
+DecodeSeg shared_seg2(const moe_problem& p, const void* h_sh, const void* w2_sh, float* y_shared) {
+    const int Is = p.I_shared;
+    DecodeSeg s = {};
+    s.A = h_sh;
+    s.lda = (int64_t)p.n_shared * Is;
+    s.uniform_rows = p.T;
+    s.B = w2_sh;
+    s.N_w = p.H;
+    s.b_group_stride = 0;
+    s.k_seg = Is;
+    s.b_seg_stride = (int64_t)p.H * Is;
+    s.K = p.n_shared * Is;
+    s.epi = EPI_F32;
+    s.out = y_shared;
+    s.ldo = p.H;
+    s.n_groups = 1;
+    s.blocks = (p.H + 31) / 32;
+    return s;
+}
+
+hipError_t run_decode(const DecodeSeg* a, const DecodeSeg* b, const int32_t* row_src, int k,
+                      const float* route_w, int w_dtype, int64_t route_count, hipStream_t s) {
+    DecodeArgs d = {};
+    d.seg[0] = a ? *a : *b;
+    d.n_seg = 1;
+    if (a && b) {
+        d.seg[1] = *b;
+        d.n_seg = 2;
+    }
+    d.row_src = row_src;
+    d.k_top = k;
+    d.route_w = route_w;
+    // Split K over a workgroup's 4 wavefronts when the launch has fewer units
+    // than the chip has wavefronts and each wavefront still gets >= 8 K groups
+    // of 64 (a longer stream per wavefront keeps its ring full).  The number of
+    // touched experts is on the device; the host bounds it by min(E, T*k).
+    int64_t units = 0;
+    int kmin = INT_MAX;
+    for (int i = 0; i < d.n_seg; ++i) {
+        const DecodeSeg& g = d.seg[i];
+        const int64_t groups = g.offsets ? std::min<int64_t>(g.n_groups, route_count) : g.n_groups;
+        units += groups * g.blocks;
+        kmin = std::min(kmin, g.K);
+    }
+    const int split = (units < (int64_t)decode_grid() * 4 && kmin >= 2048) ? 1 : 0;
+    // the shared experts are always bf16; a segment list that starts with them
+    // runs the bf16 instantiation
+    return launch_decode_gemm(d, a ? w_dtype : MOE_BF16, split, decode_grid(), s);
+}
+
 moe_status check_ptrs16(std::initializer_list<const void*> ps) {
     for (const void* q : ps)
         if (!q || !aligned16(q)) return MOE_ERR_ARG;
@@ -317,9 +455,15 @@ moe_status moe_expert_ffn(const moe_problem* p, const void* x_disp, const int32_
     if (check_ptrs16({x_disp, w13, w2, y_disp}) != MOE_OK || !offsets) return MOE_ERR_ARG;
     if ((p->w_dtype == MOE_E4M3) != (s13 != nullptr && s2 != nullptr)) return MOE_ERR_ARG;
     hipStream_t s = (hipStream_t)stream;
+    void* h = at<void>(ws, L.h);
+    if (decode_mode(*p)) {
+        const DecodeSeg g1 = routed_seg1(*p, x_disp, 0, offsets, w13, s13, h);
+        if (run_decode(&g1, nullptr, nullptr, p->k, nullptr, p->w_dtype, (int64_t)p->T * p->k, s) != hipSuccess) return MOE_ERR_HIP;
+        const DecodeSeg g2 = routed_seg2(*p, h, offsets, w2, s2, EPI_STORE, y_disp);
+        return hip_status(run_decode(&g2, nullptr, nullptr, p->k, nullptr, p->w_dtype, (int64_t)p->T * p->k, s));
+    }
     int32_t* mt = at<int32_t>(ws, L.mt_off);
     if (launch_tile_table(offsets, p->E, p->C, gemm_bm(*p), mt, s) != hipSuccess) return MOE_ERR_HIP;
-    void* h = at<void>(ws, L.h);
     if (run_gemm1(*p, x_disp, offsets, mt, w13, s13, h, s) != hipSuccess) return MOE_ERR_HIP;
     return hip_status(run_gemm2(*p, h, offsets, mt, w2, s2, EPI_STORE, y_disp, nullptr, nullptr, s));
 }
@@ -333,7 +477,15 @@ moe_status moe_shared_ffn(const moe_problem* p, const void* x, const void* w13_s
     if (p->n_shared == 0) return MOE_ERR_ARG;
     if (p->T == 0) return MOE_OK;
     if (check_ptrs16({x, w13_sh, w2_sh, y_shared}) != MOE_OK) return MOE_ERR_ARG;
-    return hip_status(run_shared(*p, x, w13_sh, w2_sh, at<void>(ws, L.h_sh), y_shared, (hipStream_t)stream));
+    hipStream_t s = (hipStream_t)stream;
+    if (decode_mode(*p)) {
+        void* h_sh = at<void>(ws, L.h_sh);
+        const DecodeSeg g1 = shared_seg1(*p, x, w13_sh, h_sh);
+        if (run_decode(nullptr, &g1, nullptr, p->k, nullptr, MOE_BF16, (int64_t)p->T * p->k, s) != hipSuccess) return MOE_ERR_HIP;
+        const DecodeSeg g2 = shared_seg2(*p, h_sh, w2_sh, y_shared);
+        return hip_status(run_decode(nullptr, &g2, nullptr, p->k, nullptr, MOE_BF16, (int64_t)p->T * p->k, s));
+    }
+    return hip_status(run_shared(*p, x, w13_sh, w2_sh, at<void>(ws, L.h_sh), y_shared, s));
 }
 
 moe_status moe_combine(const moe_problem* p, const void* y_disp, const int32_t* route_dst,
@@ -396,16 +548,35 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
                           at<int32_t>(ws, L.ctrl), s);
     if (e == hipSuccess) e = mark(m, MOE_STAGE_COUNT, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
+    const bool dec = decode_mode(P);
     if (P.T > 0)
         e = launch_scatter(x, P.T, P.H, P.k, P.E, P.C, act_bytes(P), r_max_of(P), at<int32_t>(ws, L.rexp),
                            at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), offsets, route_dst,
-                           row_src, x_disp, s);
+                           row_src, dec ? nullptr : x_disp, s);
     if (e == hipSuccess) e = mark(m, MOE_STAGE_SCATTER, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     void* h = at<void>(ws, L.h);
     void* ybuf = at<void>(ws, L.ybuf);
     float* y_sh = P.n_shared ? at<float>(ws, L.y_shared) : nullptr;
     const bool work = P.T > 0 && r_max_of(P) > 0;
+    if (dec && P.T > 0) {
+        // slot-indexed expert GEMMs; routed and shared units share each launch
+        void* h_sh = at<void>(ws, L.h_sh);
+        const DecodeSeg r1 = routed_seg1(P, x, 1, offsets, w13, s13, h);
+        const DecodeSeg sh1 = P.n_shared ? shared_seg1(P, x, w13_sh, h_sh) : DecodeSeg{};
+        e = run_decode(&r1, P.n_shared ? &sh1 : nullptr, row_src, P.k, w, P.w_dtype, (int64_t)P.T * P.k, s);
+        if (e == hipSuccess) e = mark(m, MOE_STAGE_GEMM1, s);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        const DecodeSeg r2 = routed_seg2(P, h, offsets, w2, s2, EPI_COMBINE, ybuf);
+        const DecodeSeg sh2 = P.n_shared ? shared_seg2(P, h_sh, w2_sh, y_sh) : DecodeSeg{};
+        e = run_decode(&r2, P.n_shared ? &sh2 : nullptr, row_src, P.k, w, P.w_dtype, (int64_t)P.T * P.k, s);
+        if (e == hipSuccess) e = mark(m, MOE_STAGE_GEMM2, s);
+        if (e == hipSuccess) e = mark(m, MOE_STAGE_SHARED, s);
+        if (e == hipSuccess)
+            e = launch_combine(ybuf, 0, route_dst, nullptr, y_sh, out, P.T, P.k, P.H, P.act_dtype, s);
+        if (e == hipSuccess) e = mark(m, MOE_STAGE_COMBINE, s);
+        return hip_status(e);
+    }
     if (work) e = run_gemm1(P, x_disp, offsets, mt, w13, s13, h, s);
     if (e == hipSuccess) e = mark(m, MOE_STAGE_GEMM1, s);
     if (e != hipSuccess) return MOE_ERR_HIP;

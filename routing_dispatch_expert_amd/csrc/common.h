@@ -90,6 +90,40 @@ constexpr int kGemmF32BM = 64; // rows per m-tile of the f32 kernel
 hipError_t launch_gemm_bf16(const GemmArgs& a, int w_dtype, int grid, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, int grid, hipStream_t s);
 
+// ---- slot-indexed expert GEMMs for decode-shaped batches ---------------------
+// One segment: the routed experts (offsets != null: rows offsets[g] ..
+// offsets[g+1], activation row = row_src[row] / k_top when gather, else the
+// row itself) or the shared experts (offsets == null: uniform_rows rows,
+// activation row = row).  blocks = units per group (16 output columns for
+// SwiGLU, 32 otherwise).
+struct DecodeSeg {
+    const void* A;
+    int64_t lda;
+    int gather;
+    const int32_t* offsets;
+    int uniform_rows;
+    const void* B;
+    int64_t b_group_stride;
+    int64_t b_seg_stride;
+    int k_seg;
+    const float* bscale;
+    int N_w, K, I;
+    int epi;
+    void* out;
+    int64_t ldo;
+    int64_t out_col_per_group;
+    int n_groups;
+    int blocks;
+};
+struct DecodeArgs {
+    DecodeSeg seg[2];
+    int n_seg;
+    const int32_t* row_src;
+    int k_top;
+    const float* route_w;
+};
+hipError_t launch_decode_gemm(const DecodeArgs& d, int w_dtype, int split, int grid, hipStream_t s);
+
 // ---- combine -----------------------------------------------------------------
 // out[t] = sum_j (route_dst >= 0) coef * y[src] (+ y_shared[t]); NaN row when a
 // route of t is malformed.  gather: src = route_dst[q], coef = w[q];

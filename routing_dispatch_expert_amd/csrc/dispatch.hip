@@ -217,6 +217,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(
          r += (int64_t)gridDim.x * blockDim.x)
         row_src[r] = -1;
     __syncthreads();
+    if (x_disp == nullptr) return;  // metadata only (slot-indexed expert GEMMs read x in place)
     const V* src = x + (int64_t)t * H_vec;
     for (int c = tid; c < H_vec; c += blockDim.x) {
         const V v = src[c];

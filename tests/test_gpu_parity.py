@@ -1,5 +1,8 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
+Batches with at most 12 routes per expert on average run the slot-indexed
+expert GEMMs; the others run the tiled grouped GEMM; both are covered.
+
 Each test prints the case it runs before touching the GPU.  Small cases are
 compared element by element against the full oracle; they span several
 128-row m-tiles with a ragged last tile, several k-tiles and n-tiles.  The
@@ -31,6 +34,10 @@ SMALL = {
     # hidden / intermediate not multiples of the 256-column tile
     "ragged_n_relu2": ("relu2_distinct_R8", dict(H=384, I=384)),
     "ragged_n_swiglu": ("prefill_T256", dict(T=300, H=384, E=4, k=2, I=384, C=300)),
+    # decode-shaped (few rows per expert): slot-indexed expert GEMMs
+    "decode_fp8": ("skewed_fp8", dict(T=16, H=256, E=32, k=4, I=256, C=16)),
+    "decode_rows_over_32": ("skewed_bf16", dict(T=180, H=256, E=32, k=2, I=128, C=180)),
+    "decode_shared_T64": ("decode_T32", dict(T=64, H=256, I=128, I_shared=256, C=64)),
 }
 # Full-size workloads.
 FULL = ["tiny_fp32", "prefill_T256", "prefill_T2048", "prefill_T8192", "decode_T1", "decode_T8",
