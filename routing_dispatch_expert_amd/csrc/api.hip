@@ -117,12 +117,16 @@ int gemm_grid(int64_t tiles_upper) {
     return g > 8 ? g : 8;
 }
 
-// GEMM1 (x_disp -> h) over the routed experts, tile table mt_off.
-hipError_t run_gemm1(const moe_problem& p, const void* x_disp, const int32_t* offsets,
+// GEMM1 (A -> h) over the routed experts, tile table mt_off.  A is x_disp,
+// or x in token order read through row_src when row_src is given (bf16).
+hipError_t run_gemm1(const moe_problem& p, const void* A, const int32_t* offsets,
                      const int32_t* mt_off, const void* w13, const float* s13, void* h,
-                     hipStream_t s) {
+                     hipStream_t s, const int32_t* row_src = nullptr) {
     GemmArgs a = {};
-    a.A = x_disp;
+    a.A = A;
+    a.row_src = row_src;
+    a.gather = row_src != nullptr;
+    a.k_top = p.k;
     a.lda = p.H;
     a.B = w13;
     a.N_w = p.act == MOE_SWIGLU ? 2 * p.I : p.I;
@@ -549,10 +553,12 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
     if (e == hipSuccess) e = mark(m, MOE_STAGE_COUNT, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     const bool dec = decode_mode(P);
+    // bf16 layers read expert rows in place (no expert-contiguous copy of x)
+    const bool in_place = dec || P.act_dtype == MOE_BF16;
     if (P.T > 0)
         e = launch_scatter(x, P.T, P.H, P.k, P.E, P.C, act_bytes(P), r_max_of(P), at<int32_t>(ws, L.rexp),
                            at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), offsets, route_dst,
-                           row_src, dec ? nullptr : x_disp, s);
+                           row_src, in_place ? nullptr : x_disp, s);
     if (e == hipSuccess) e = mark(m, MOE_STAGE_SCATTER, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     void* h = at<void>(ws, L.h);
@@ -577,7 +583,9 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
         if (e == hipSuccess) e = mark(m, MOE_STAGE_COMBINE, s);
         return hip_status(e);
     }
-    if (work) e = run_gemm1(P, x_disp, offsets, mt, w13, s13, h, s);
+    if (work)
+        e = in_place ? run_gemm1(P, x, offsets, mt, w13, s13, h, s, row_src)
+                     : run_gemm1(P, x_disp, offsets, mt, w13, s13, h, s);
     if (e == hipSuccess) e = mark(m, MOE_STAGE_GEMM1, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (work) e = run_gemm2(P, h, offsets, mt, w2, s2, EPI_COMBINE, ybuf, w, row_src, s);

@@ -80,8 +80,10 @@ struct GemmArgs {
     int64_t ldo;
     int64_t out_col_per_group;  // column offset added per group (concatenated h)
     const float* route_w;       // EPI_COMBINE
-    const int32_t* row_src;     // EPI_COMBINE
+    const int32_t* row_src;     // EPI_COMBINE; with gather, also the A-row map
     int I;                      // EPI_SWIGLU: up rows start at I in B
+    int gather;                 // A row r is row row_src[r] / k_top of A (x in token order)
+    int k_top;
 };
 
 constexpr int kGemmBM = 256;   // rows per m-tile of the bf16 MFMA kernel

@@ -8,7 +8,9 @@
 // Both projections are "NT" products: activations A [rows, K] and weights
 // B [N, K] both have K contiguous, C = A B^T.  Rows of one expert are
 // contiguous in A (count-first dispatch), so an expert's work is a run of
-// m-tiles; the m-tile prefix over experts (mt_off, built on the device by the
+// m-tiles.  With `gather`, the gate/up projection reads each row of an expert
+// straight from the token-ordered input (row r is token row_src[r] / k), so
+// the expert-contiguous copy of the input is never written; the m-tile prefix over experts (mt_off, built on the device by the
 // dispatch) maps a tile index to its expert with a binary search in LDS.
 // Empty experts own no tiles; an overflowing expert owns ceil(C / BM).  The
 // grid is persistent: each workgroup strides over tile indices, so the grid
@@ -226,8 +228,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         };
         // per-thread global byte offsets (k = 0) of its DMA sources
         const int ra0 = wave * 32 + dr, ra1 = ra0 + 16;
-        const int64_t ga0 = (int64_t)(a_row0 + min(ra0, rows - 1)) * a.lda * 2 + ((ds ^ swz(ra0)) * 16);
-        const int64_t ga1 = (int64_t)(a_row0 + min(ra1, rows - 1)) * a.lda * 2 + ((ds ^ swz(ra1)) * 16);
+        int64_t ar0 = a_row0 + min(ra0, rows - 1), ar1 = a_row0 + min(ra1, rows - 1);
+        if (a.gather) {  // expert rows read in place: the token of each route
+            ar0 = a.row_src[ar0] / a.k_top;
+            ar1 = a.row_src[ar1] / a.k_top;
+        }
+        const int64_t ga0 = ar0 * a.lda * 2 + ((ds ^ swz(ra0)) * 16);
+        const int64_t ga1 = ar1 * a.lda * 2 + ((ds ^ swz(ra1)) * 16);
         const int64_t gbase = (int64_t)g * a.b_group_stride;
         int64_t gb0, gb1 = 0;
         if (FP8) {
