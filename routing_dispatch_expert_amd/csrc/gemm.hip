@@ -17,13 +17,13 @@
 // never depends on the routing and no host synchronisation is needed.
 //
 // bf16 kernel: 512 threads = 8 waves, block tile BM x BN x BK =
-// 256 x 256 x 64, wave tile 128 x 64 = 4 x 2 MFMA v_mfma_f32_32x32x16_bf16
-// blocks, one workgroup per CU (two LDS stages of A and B, ~147 KB of the
-// 160 KB LDS).  Operands are staged global -> registers -> LDS (rows padded
-// to 72 elements, so the 16-byte fragment reads of 8 consecutive rows hit
-// distinct banks); the next k-tile's global loads are in flight while the
-// current one is multiplied, with one barrier per k-tile.  A wave skips the
-// MFMAs of 32-row blocks that lie past the end of its expert's rows.
+// 256 x 256 x 32, wave tile 128 x 64 = 4 x 2 MFMA v_mfma_f32_32x32x16_bf16
+// blocks, one workgroup per CU.  Operands go straight from global memory to
+// a 4-stage LDS ring (global_load_lds_dwordx4), three k-tiles in flight
+// while one is multiplied, one barrier per k-tile; rows of 64 bytes with an
+// XOR chunk swizzle keep the fragment reads free of bank conflicts.  Rows of
+// a tile past the end of its expert cost neither loads (16-row groups) nor
+// MFMAs (32-row blocks).
 //
 // SwiGLU needs gate and up of the same output column in the same lane: the
 // B tile of a wave column holds 32 gate rows then the 32 matching up rows,
@@ -123,21 +123,20 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
         : "memory");
 }
 
-// Wait until at most n of this thread's vector-memory operations are
-// outstanding (n known at compile time per case), then workgroup barrier.
-// No memory fence: LDS written by global_load_lds is complete once the
-// issuing thread's vmcnt has dropped past it.
+// Wait until at most 2L / L / 0 of this thread's vector-memory operations are
+// outstanding (two, one or no later k-tiles still in flight, L = the thread's
+// DMA instructions per k-tile), then workgroup barrier.  No memory fence: LDS
+// written by global_load_lds is complete once the issuing thread's vmcnt has
+// dropped past it.
+template <int N>
+__device__ __forceinline__ void waitcnt_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 template <int L>
 __device__ __forceinline__ void wait_tiles_barrier(int tiles_after) {
-    if (tiles_after >= 2) {
-        if (L == 4) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    } else if (tiles_after == 1) {
-        if (L == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    } else {
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
+    if (tiles_after >= 2) waitcnt_barrier<2 * L>();
+    else if (tiles_after == 1) waitcnt_barrier<L>();
+    else waitcnt_barrier<0>();
 }
 
 __device__ __forceinline__ void barrier_lds() {
@@ -159,7 +158,7 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint2 v) {
 template <int EPI, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int B_STAGE = FP8 ? B_STAGE_E4M3 : B_STAGE_BF16;
-    constexpr int L = FP8 ? 3 : 4;  // DMA instructions per thread per k-tile
+    constexpr int LB = FP8 ? 1 : 2;  // B DMA instructions per thread per k-tile
     __shared__ __attribute__((aligned(1024))) unsigned char sA[kStages][A_STAGE];
     __shared__ __attribute__((aligned(1024))) unsigned char sB[kStages][B_STAGE];
     __shared__ int32_t s_mt[kMaxGroupsLds + 1];
@@ -190,10 +189,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     const char* Bb = (const char*)a.B;
     const int nk = a.K / BK;
 
-    // DMA plan.  A: wave w fills rows w*32 + 16*b + lane/4 (b = 0, 1).
+    // DMA plan.  A: wave w fills the 16-row groups w and w + 8 (row
+    // 16*group + lane/4); a group wholly past the expert's last row is not
+    // loaded, so a half-filled tile issues half the A traffic and every wave
+    // still has one A group while rows > 128.  bf16 B: wave w fills rows
+    // w*32 + 16*b + lane/4 (b = 0, 1).  e4m3 B: wave w fills rows w*32 +
+    // lane/2, 16-byte half lane%2 (one instruction per k-tile).
     const int dr = lane >> 2, ds = lane & 3;
-    // bf16 B: same shape as A.  e4m3 B: wave w fills rows w*32 + lane/2,
-    // 16-byte half lane%2 (one instruction per k-tile).
 
     for (int64_t Lt = vid; Lt < total; Lt += G) {
         int g, cnt, ml, nt;
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
             return min(nt * BN + r, a.N_w - 1);   // rows past N (ragged last tile): clamped
         };
         // per-thread global byte offsets (k = 0) of its DMA sources
-        const int ra0 = wave * 32 + dr, ra1 = ra0 + 16;
+        const int ra0 = wave * 16 + dr, ra1 = ra0 + 128;
         int64_t ar0 = a_row0 + min(ra0, rows - 1), ar1 = a_row0 + min(ra1, rows - 1);
         if (a.gather) {  // expert rows read in place: the token of each route
             ar0 = a.row_src[ar0] / a.k_top;
@@ -241,11 +243,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
             const int rb = wave * 32 + (lane >> 1), hb = lane & 1;
             gb0 = (gbase + (int64_t)brow_of(rb) * a.k_seg) + ((hb ^ ((rb >> 2) & 1)) * 16);
         } else {
-            gb0 = (gbase + (int64_t)brow_of(ra0) * a.k_seg) * 2 + ((ds ^ swz(ra0)) * 16);
-            gb1 = (gbase + (int64_t)brow_of(ra1) * a.k_seg) * 2 + ((ds ^ swz(ra1)) * 16);
+            const int rb0 = wave * 32 + dr, rb1 = rb0 + 16;
+            gb0 = (gbase + (int64_t)brow_of(rb0) * a.k_seg) * 2 + ((ds ^ swz(rb0)) * 16);
+            gb1 = (gbase + (int64_t)brow_of(rb1) * a.k_seg) * 2 + ((ds ^ swz(rb1)) * 16);
         }
         // wave-uniform LDS bases of this wave's DMA blocks in stage 0
-        const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(sA[0]) + wave * 2048);
+        const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(sA[0]) + wave * 1024);
         const uint32_t lb0 = __builtin_amdgcn_readfirstlane(lds_addr(sB[0]) + wave * (FP8 ? 1024 : 2048));
         // K order: the tile starts at k-tile `rot` and wraps.  Tiles running at
         // the same time then read different column offsets of their rows, so
@@ -254,7 +257,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         // expert and the n-tile, so a row's summation order never depends on
         // the other tokens of the batch.
         const int rot = (g * 7 + nt * 13) % nk;
-        auto issue = [&](int kt) {
+        // LA = A groups this wave loads (0, 1 or 2; wave-uniform)
+        auto issue = [&](auto la_c, int kt) {
+            constexpr int LA = decltype(la_c)::value;
             const int slot = kt % kStages;
             int kr = kt + rot;
             if (kr >= nk) kr -= nk;
@@ -262,8 +267,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
             const int seg = k0 / a.k_seg;
             const int64_t bo = (int64_t)seg * a.b_seg_stride + (k0 - seg * a.k_seg);
             const uint32_t la = la0 + slot * A_STAGE, lb = lb0 + slot * B_STAGE;
-            dma16(Ab + ga0 + (int64_t)k0 * 2, la);
-            dma16(Ab + ga1 + (int64_t)k0 * 2, la + 1024);
+            if (LA >= 1) dma16(Ab + ga0 + (int64_t)k0 * 2, la);
+            if (LA >= 2) dma16(Ab + ga1 + (int64_t)k0 * 2, la + 8192);
             if (FP8) {
                 dma16(Bb + gb0 + bo, lb);
             } else {
@@ -287,17 +292,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
             col_ok ? max(0, min(4, (rows - 32 * wm + 63) / 64)) : 0);
 
         barrier_lds();  // the previous tile's last stage is no longer read
-#pragma unroll
-        for (int st = 0; st < kStages - 1; ++st)
-            if (st < nk) issue(st);
 
         const int rA = lane & 31, half = lane >> 5;
-        // the pipelined k-loop, specialised on the number NA of active row blocks
-        auto kloop = [&](auto na_c) {
+        // the pipelined k-loop, specialised on the number NA of active row
+        // blocks of the wave's MFMAs and the number LA of A groups it loads
+        auto kloop = [&](auto na_c, auto la_c) {
             constexpr int NA = decltype(na_c)::value;
+            constexpr int LA = decltype(la_c)::value;
+#pragma unroll
+            for (int st = 0; st < kStages - 1; ++st)
+                if (st < nk) issue(la_c, st);
             for (int kt = 0; kt < nk; ++kt) {
-                wait_tiles_barrier<L>(min(kStages - 2, nk - 1 - kt));
-                if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
+                wait_tiles_barrier<LB + LA>(min(kStages - 2, nk - 1 - kt));
+                if (kt + kStages - 1 < nk) issue(la_c, kt + kStages - 1);
                 if (NA == 0) continue;
                 const unsigned char* sa = sA[kt % kStages];
                 const unsigned char* sb = sB[kt % kStages];
@@ -329,12 +336,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
                 }
             }
         };
+        const int n_la = __builtin_amdgcn_readfirstlane((16 * wave < rows) + (16 * (wave + 8) < rows));
+        auto by_la = [&](auto na_c) {
+            if (n_la == 2) kloop(na_c, std::integral_constant<int, 2>{});
+            else if (n_la == 1) kloop(na_c, std::integral_constant<int, 1>{});
+            else kloop(na_c, std::integral_constant<int, 0>{});
+        };
         switch (n_act) {
-            case 4: kloop(std::integral_constant<int, 4>{}); break;
-            case 3: kloop(std::integral_constant<int, 3>{}); break;
-            case 2: kloop(std::integral_constant<int, 2>{}); break;
-            case 1: kloop(std::integral_constant<int, 1>{}); break;
-            default: kloop(std::integral_constant<int, 0>{}); break;
+            case 4: by_la(std::integral_constant<int, 4>{}); break;
+            case 3: by_la(std::integral_constant<int, 3>{}); break;
+            case 2: by_la(std::integral_constant<int, 2>{}); break;
+            case 1: by_la(std::integral_constant<int, 1>{}); break;
+            default: by_la(std::integral_constant<int, 0>{}); break;
         }
 
         // ---- epilogue: lane owns row (lane % 32) of each active row block and
