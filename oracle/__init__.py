@@ -51,6 +51,10 @@ def lib():
         L.oracle_round_bf16.argtypes = [C.c_double]
         L.oracle_route.restype = _i
         L.oracle_route.argtypes = [_i, _i, _i, _i, _p, _p, _p]
+        L.oracle_route_sigmoid.restype = _i
+        L.oracle_route_sigmoid.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p]
+        L.oracle_route_scored.restype = _i
+        L.oracle_route_scored.argtypes = [_i, _i, _i, _i, _i, C.c_double, _p, _p, _p, _p]
         L.oracle_dispatch.restype = _i64
         L.oracle_dispatch.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _i64, _p, _p]
         L.oracle_gather_rows.restype = None
@@ -60,7 +64,7 @@ def lib():
         L.oracle_combine.restype = None
         L.oracle_combine.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p]
         L.oracle_forward.restype = _i64
-        L.oracle_forward.argtypes = [_i] * 12 + [_p] * 10 + [_p] * 7
+        L.oracle_forward.argtypes = [_i] * 13 + [C.c_double] + [_p] * 11 + [_p] * 7
         _lib = L
     return _lib
 
@@ -109,12 +113,24 @@ def round_bf16(v: float) -> float:
 
 # ---- steps ---------------------------------------------------------------
 
-def route(logits: np.ndarray, k: int, renormalize: int = 0):
+SOFTMAX = 0
+SIGMOID = 1
+
+
+def route(logits: np.ndarray, k: int, renormalize: int = 0, score_func: int = SOFTMAX,
+          bias: Optional[np.ndarray] = None, route_scale: float = 1.0):
+    """ids [T,k] int32 and w [T,k] float64 of softmax (default) or sigmoid
+    routing; `bias` is the float32 selection-only correction of sigmoid
+    routing, `route_scale` multiplies every weight."""
     logits = np.ascontiguousarray(logits, dtype=np.float32)
     T, E = logits.shape
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        assert bias.shape == (E,)
     ids = np.zeros((T, k), np.int32)
     w = np.zeros((T, k), np.float64)
-    rc = lib().oracle_route(T, E, k, renormalize, _ptr(logits), _ptr(ids), _ptr(w))
+    rc = lib().oracle_route_scored(T, E, k, score_func, renormalize, route_scale,
+                                   _ptr(logits), _ptr(bias), _ptr(ids), _ptr(w))
     assert rc == 0
     return ids, w
 
@@ -180,7 +196,7 @@ def combine(route_dst: np.ndarray, w: np.ndarray, y: np.ndarray,
 
 
 def forward(cs, x, logits, w13, w2, s13=None, s2=None, w13_sh=None, w2_sh=None,
-            ids_in=None, w_in=None):
+            ids_in=None, w_in=None, score_bias=None):
     """The whole layer for case `cs` (a synth.Case); arrays in oracle storage
     convention.  Returns a dict with ids, w, counts, offsets, row_src,
     route_dst, out (float64), n_bad and the wall time in seconds."""
@@ -194,8 +210,10 @@ def forward(cs, x, logits, w13, w2, s13=None, s2=None, w13_sh=None, w2_sh=None,
     route_dst = np.zeros((T, k), np.int32)
     out = np.zeros((T, H), np.float64)
     arrs = [np.ascontiguousarray(a) if a is not None else None
-            for a in (x, logits, ids_in, w_in, w13, w2, s13, s2, w13_sh, w2_sh)]
-    x, logits, ids_in, w_in, w13, w2, s13, s2, w13_sh, w2_sh = arrs
+            for a in (x, logits, ids_in, w_in, w13, w2, s13, s2, w13_sh, w2_sh, score_bias)]
+    x, logits, ids_in, w_in, w13, w2, s13, s2, w13_sh, w2_sh, score_bias = arrs
+    if score_bias is not None:
+        score_bias = score_bias.astype(np.float32)
     if ids_in is not None:
         ids_in = ids_in.astype(np.int32)
         w_in = w_in.astype(np.float64)
@@ -204,7 +222,8 @@ def forward(cs, x, logits, w13, w2, s13=None, s2=None, w13_sh=None, w2_sh=None,
     t0 = time.perf_counter()
     n_bad = lib().oracle_forward(
         T, H, E, k, I, Cc, cs.act, fmt_of(x), fmt_of(w13), cs.n_shared, cs.I_shared,
-        cs.renormalize, _ptr(x), _ptr(logits), _ptr(ids_in), _ptr(w_in), _ptr(w13),
+        cs.renormalize, cs.score_func, cs.route_scale, _ptr(x), _ptr(logits),
+        _ptr(score_bias), _ptr(ids_in), _ptr(w_in), _ptr(w13),
         _ptr(w2), _ptr(s13), _ptr(s2), _ptr(w13_sh), _ptr(w2_sh),
         _ptr(ids), _ptr(w), _ptr(counts), _ptr(offsets), _ptr(row_src), _ptr(route_dst),
         _ptr(out))
@@ -219,4 +238,4 @@ def inputs_numpy(inp):
     conv = lambda t: None if t is None else from_torch(t)
     return dict(x=conv(inp.x), logits=conv(inp.logits), w13=conv(inp.w13), w2=conv(inp.w2),
                 s13=conv(inp.s13), s2=conv(inp.s2), w13_sh=conv(inp.w13_sh),
-                w2_sh=conv(inp.w2_sh))
+                w2_sh=conv(inp.w2_sh), score_bias=conv(inp.score_bias))

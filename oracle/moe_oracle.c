@@ -14,6 +14,9 @@
  *
  * The steps, in the order of the layer:
  *   1. softmax top-k routing              oracle_route
+ *      or sigmoid top-k routing with a     oracle_route_sigmoid
+ *      selection-only correction bias
+ *      (either one, then the route scale:  oracle_route_scored)
  *   2. count-first dispatch metadata       oracle_dispatch
  *      (counts, prefix sums, rows at known offsets; the afdEP count-first
  *      validation record, "change" and the fault list naming late counts,
@@ -32,6 +35,7 @@
 
 enum { O_F32 = 0, O_BF16 = 1, O_E4M3 = 2 };
 enum { O_SWIGLU = 0, O_RELU2 = 1 };
+enum { O_SOFTMAX = 0, O_SIGMOID = 1 };
 
 /* ---- storage formats ------------------------------------------------- */
 
@@ -132,6 +136,73 @@ int oracle_route(int T, int E, int k, int renormalize, const float *logits,
         }
     }
     free(taken);
+    return 0;
+}
+
+/* ---- 1b. sigmoid top-k routing with a correction bias ------------------ */
+
+/* Sigmoid routing (PR 33963, Description and the commit adding "projected
+ * sigmoid routing"): each expert gets the score s_e = sigma(l_e) =
+ * 1 / (1 + e^-l_e); a float32 correction bias b_e enters the selection only.
+ * Readings where the pages leave the step open:
+ *   - the selection key is a float32: s_e is sigma rounded once to float32,
+ *     and key_e = s_e + b_e is a float32 addition (the pages fix an FP32
+ *     bias; the comparison is then done in the precision the bias lives in);
+ *   - the k largest keys are taken, slot 0 first, ties to the lower index,
+ *     NaN below every number (as for softmax routing);
+ *   - the weights come from the unbiased scores: w[t,j] = sigma(l_id) (no
+ *     renormalize) or sigma(l_id) / sum over the selected sigma (renormalize),
+ *     in double;
+ *   - `bias` may be NULL (no correction).
+ * A NaN logit gets a NaN score and ranks last. */
+int oracle_route_sigmoid(int T, int E, int k, int renormalize, const float *logits,
+                         const float *bias, int32_t *ids, double *w) {
+    float *key = (float *)malloc(sizeof(float) * (size_t)(E > 0 ? E : 1));
+    unsigned char *taken = (unsigned char *)malloc((size_t)(E > 0 ? E : 1));
+    if (!key || !taken) { free(key); free(taken); return -1; }
+    for (int t = 0; t < T; ++t) {
+        const float *l = logits + (int64_t)t * E;
+        for (int e = 0; e < E; ++e) {
+            float s = (float)(1.0 / (1.0 + exp(-(double)l[e])));
+            float b = bias ? bias[e] : 0.0f;
+            volatile float sum = s + b;   /* one float32 rounding */
+            key[e] = bias ? sum : s;
+        }
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || ranks_before(key[e], e, key[best], best)) best = e;
+            }
+            taken[best] = 1;
+            ids[(int64_t)t * k + j] = best;
+        }
+        double ssel = 0.0;
+        for (int j = 0; j < k; ++j)
+            ssel += 1.0 / (1.0 + exp(-(double)l[ids[(int64_t)t * k + j]]));
+        for (int j = 0; j < k; ++j) {
+            double sj = 1.0 / (1.0 + exp(-(double)l[ids[(int64_t)t * k + j]]));
+            w[(int64_t)t * k + j] = renormalize ? sj / ssel : sj;
+        }
+    }
+    free(key);
+    free(taken);
+    return 0;
+}
+
+/* Either router, then every weight times `route_scale` (the route scaling
+ * the sigmoid-routing commit of PR 33963 keeps; 1 for plain softmax
+ * routing).  `bias` is only meaningful for sigmoid routing. */
+int oracle_route_scored(int T, int E, int k, int score_func, int renormalize,
+                        double route_scale, const float *logits, const float *bias,
+                        int32_t *ids, double *w) {
+    int rc = score_func == O_SIGMOID
+                 ? oracle_route_sigmoid(T, E, k, renormalize, logits, bias, ids, w)
+                 : oracle_route(T, E, k, renormalize, logits, ids, w);
+    if (rc != 0) return rc;
+    if (route_scale != 1.0)
+        for (int64_t q = 0; q < (int64_t)T * k; ++q) w[q] *= route_scale;
     return 0;
 }
 
@@ -294,7 +365,8 @@ static int64_t fmt_bytes(int fmt) { return fmt == O_F32 ? 4 : (fmt == O_BF16 ? 2
  * Returns the number of malformed routes, or a negative value on failure. */
 int64_t oracle_forward(int T, int H, int E, int k, int I, int C, int act,
                        int x_fmt, int w_fmt, int n_shared, int I_shared,
-                       int renormalize, const void *x, const float *logits,
+                       int renormalize, int score_func, double route_scale,
+                       const void *x, const float *logits, const float *score_bias,
                        const int32_t *ids_in, const double *w_in,
                        const void *w13, const void *w2, const float *s13,
                        const float *s2, const void *w13_sh, const void *w2_sh,
@@ -308,7 +380,8 @@ int64_t oracle_forward(int T, int H, int E, int k, int I, int C, int act,
     if (ids_in) {
         memcpy(ids, ids_in, sizeof(int32_t) * (size_t)nq);
         memcpy(w, w_in, sizeof(double) * (size_t)nq);
-    } else if (oracle_route(T, E, k, renormalize, logits, ids, w) != 0) {
+    } else if (oracle_route_scored(T, E, k, score_func, renormalize, route_scale, logits,
+                                   score_bias, ids, w) != 0) {
         return -2;
     }
     uint8_t *bad = (uint8_t *)malloc((size_t)(T > 0 ? T : 1));

@@ -40,8 +40,11 @@ ACT_RELU2 = 1
 FMT_F32 = 0
 FMT_BF16 = 1
 FMT_E4M3 = 2
+SCORE_SOFTMAX = 0
+SCORE_SIGMOID = 1
 
-_TENSOR_IDS = {"x": 1, "logits": 2, "w13": 3, "w2": 4, "w13_sh": 5, "w2_sh": 6}
+_TENSOR_IDS = {"x": 1, "logits": 2, "w13": 3, "w2": 4, "w13_sh": 5, "w2_sh": 6,
+               "score_bias": 7}
 
 
 @dataclass(frozen=True)
@@ -63,6 +66,9 @@ class Case:
     n_shared: int = 0
     I_shared: int = 0
     renormalize: int = 0
+    score_func: int = SCORE_SOFTMAX    # sigmoid: selection on sigmoid + bias
+    route_scale: float = 1.0           # multiplies every routing weight
+    bias_std: float = 0.0              # sigmoid correction bias N(0, bias_std^2); 0 = none
     logits_kind: str = "normal"        # normal | pm16_shared | pm16_distinct | zipf
     zipf_s: float = 1.1
     w_std: float = 0.02
@@ -102,6 +108,15 @@ def _cases() -> Dict[str, Case]:
                             C=512, logits_kind="zipf")
     c["skewed_fp8"] = replace(c["skewed_bf16"], name="skewed_fp8",
                               w_fmt=FMT_E4M3)
+    # Sigmoid routing with a float32 selection-only correction bias and
+    # normalised, scaled weights, on the ReLU-square expert shape (16 rows)
+    # and on the 2048-token prefill shape.
+    c["sigmoid_relu2_R16"] = Case("sigmoid_relu2_R16", T=16, H=1024, E=240, k=9, I=1536,
+                                  C=16, act=ACT_RELU2, score_func=SCORE_SIGMOID,
+                                  renormalize=1, route_scale=2.5, bias_std=0.1)
+    c["sigmoid_T2048"] = replace(c["prefill_T2048"], name="sigmoid_T2048",
+                                 score_func=SCORE_SIGMOID, renormalize=1,
+                                 route_scale=2.5, bias_std=0.1)
     return c
 
 
@@ -165,6 +180,13 @@ def make_logits(cs: Case, device="cpu") -> torch.Tensor:
     raise ValueError(cs.logits_kind)
 
 
+def make_score_bias(cs: Case, device="cpu") -> Optional[torch.Tensor]:
+    """float32 [E] correction bias of sigmoid routing, or None."""
+    if cs.score_func != SCORE_SIGMOID or cs.bias_std == 0.0:
+        return None
+    return _normal((cs.E,), cs.bias_std, cs.seed, "score_bias", -1, device)
+
+
 def make_x(cs: Case, device="cpu") -> torch.Tensor:
     return _store(_normal((cs.T, cs.H), cs.x_std, cs.seed, "x", -1, device),
                   cs.act_fmt)
@@ -196,12 +218,13 @@ class Inputs:
     s2: Optional[torch.Tensor] = None
     w13_sh: Optional[torch.Tensor] = None
     w2_sh: Optional[torch.Tensor] = None
+    score_bias: Optional[torch.Tensor] = None
 
     def to(self, device) -> "Inputs":
         mv = lambda t: None if t is None else t.to(device)
         return Inputs(self.case, mv(self.x), mv(self.logits), mv(self.w13),
                       mv(self.w2), mv(self.s13), mv(self.s2), mv(self.w13_sh),
-                      mv(self.w2_sh))
+                      mv(self.w2_sh), mv(self.score_bias))
 
 
 def make_inputs(cs: Case, device="cpu", experts: Optional[List[int]] = None) -> Inputs:
@@ -233,7 +256,7 @@ def make_inputs(cs: Case, device="cpu", experts: Optional[List[int]] = None) -> 
         sh = [make_expert_weights(cs, s, device, shared=True) for s in range(cs.n_shared)]
         w13_sh = torch.stack([a for a, _, _, _ in sh]).contiguous()
         w2_sh = torch.stack([b for _, b, _, _ in sh]).contiguous()
-    return Inputs(cs, x, logits, w13, w2, s13, s2, w13_sh, w2_sh)
+    return Inputs(cs, x, logits, w13, w2, s13, s2, w13_sh, w2_sh, make_score_bias(cs, device))
 
 
 def bad_routes(T: int, k: int, E: int, kind: str, seed: int = 0) -> torch.Tensor:

@@ -130,6 +130,100 @@ def test_softmax_against_longdouble_and_scipy():
                                    rtol=1e-12)
 
 
+# ---- sigmoid routing with a selection-only correction bias -----------------
+
+def test_sigmoid_bias_selects_but_does_not_weight():
+    # equal logits give every expert the score sigma(0) = 1/2 exactly, so the
+    # selection is decided by the bias alone (grid values: 1/2 + b is exact in
+    # float32, ties included) while the weights stay those of equal scores
+    rng = np.random.default_rng(21)
+    for E, k in ((8, 3), (16, 5), (64, 6), (240, 9)):
+        lg = np.zeros((6, E), np.float32)
+        b = (rng.integers(-64, 65, size=E) / 256.0).astype(np.float32)
+        want = list(np.argsort(-b, kind="stable")[:k])
+        ids, w = oracle.route(lg, k, 0, oracle.SIGMOID, b)
+        assert all(list(r) == want for r in ids)
+        assert np.all(w == 0.5)
+        _, wn = oracle.route(lg, k, 1, oracle.SIGMOID, b, 2.5)
+        np.testing.assert_allclose(wn, 2.5 / k, rtol=4e-16)
+
+
+def test_sigmoid_pm16_with_small_bias_orders_within_the_selected_set():
+    # +16 on the selected set, -16 elsewhere: a bias of magnitude < 1/2 cannot
+    # change the set (sigma(16) - sigma(-16) > 0.99) but orders it; the
+    # normalised weights are 1/k whatever the order
+    rng = np.random.default_rng(22)
+    E, k = 240, 9
+    lg = np.full((4, E), -16.0, np.float32)
+    for t in range(4):
+        lg[t, 9 * t:9 * t + 9] = 16.0
+    b = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    ids, w = oracle.route(lg, k, 1, oracle.SIGMOID, b)
+    for t in range(4):
+        sel = np.arange(9 * t, 9 * t + 9)
+        key = np.float32(scipy.special.expit(16.0)) + b[sel]
+        assert list(ids[t]) == list(sel[np.argsort(-key, kind="stable")])
+    np.testing.assert_allclose(w, 1.0 / k, rtol=4e-16)
+
+
+def test_sigmoid_scores_against_expit_with_float32_ties():
+    # logits up to +-30: sigma rounds to 1.0f (or to denormal-free tiny values)
+    # for many experts, so the float32 keys tie and the lower index must win;
+    # the weights are the unrounded scores
+    rng = np.random.default_rng(23)
+    lg = (rng.standard_normal((40, 128)) * 12).astype(np.float32)
+    ids, w = oracle.route(lg, 8, 0, oracle.SIGMOID)
+    s = scipy.special.expit(lg.astype(np.float64))
+    key = s.astype(np.float32)
+    n_tied = 0
+    for t in range(40):
+        want = np.argsort(-key[t], kind="stable")[:8]
+        assert list(ids[t]) == list(want)
+        np.testing.assert_allclose(w[t], s[t, want], rtol=1e-15)
+        n_tied += int((key[t, want] == np.float32(1.0)).sum() > 1)
+    assert n_tied > 10   # the case really exercises ties
+    # a different order from the raw-logit top-k somewhere (ties resolved by index)
+    assert any(list(ids[t]) != list(np.argsort(-lg[t], kind="stable")[:8]) for t in range(40))
+
+
+def test_sigmoid_topk_bruteforce_with_nan_inf_and_bias():
+    pool = np.array([-1.0, 0.0, 1.0, -np.inf, np.inf, np.nan, 2.5, 40.0], np.float32)
+    bpool = np.array([0.0, 0.25, -0.25, 0.5], np.float32)
+    rng = np.random.default_rng(24)
+    for E in range(1, 8):
+        for k in range(1, min(E, 4) + 1):
+            for _ in range(30):
+                lg = rng.choice(pool, size=(1, E)).astype(np.float32)
+                b = rng.choice(bpool, size=E).astype(np.float32)
+                ids, w = oracle.route(lg, k, 0, oracle.SIGMOID, b)
+                with np.errstate(over="ignore"):
+                    sc = scipy.special.expit(lg[0].astype(np.float64))
+                key = [float(np.float32(np.float32(v) + bb)) for v, bb in zip(sc, b)]
+                winners = []
+                for S in itertools.combinations(range(E), k):
+                    worst = max(_order_key(key[i], i) for i in S)
+                    if all(_order_key(key[o], o) > worst for o in range(E) if o not in S):
+                        winners.append(S)
+                assert len(winners) == 1
+                want = sorted(winners[0], key=lambda i: _order_key(key[i], i))
+                assert list(ids[0]) == want, (lg, b, ids, want)
+                np.testing.assert_allclose(w[0], sc[want], rtol=1e-15)
+
+
+def test_route_scale_and_renormalised_sum():
+    rng = np.random.default_rng(25)
+    lg = rng.standard_normal((30, 64)).astype(np.float32)
+    b = (rng.standard_normal(64) * 0.1).astype(np.float32)
+    for sf, bias in ((oracle.SOFTMAX, None), (oracle.SIGMOID, b)):
+        i1, w1 = oracle.route(lg, 6, 1, sf, bias)
+        i2, w2 = oracle.route(lg, 6, 1, sf, bias, 2.5)
+        np.testing.assert_array_equal(i1, i2)
+        np.testing.assert_allclose(w2, 2.5 * w1, rtol=2e-16)
+        np.testing.assert_allclose(w2.sum(axis=1), 2.5, rtol=1e-14)
+        i4, w4 = oracle.route(lg, 6, 0, sf, bias, 4.0)
+        np.testing.assert_array_equal(w4, 4.0 * oracle.route(lg, 6, 0, sf, bias)[1])
+
+
 def test_all_minus_inf_row_poisons_weights():
     lg = np.full((2, 8), -np.inf, np.float32)
     lg[1] = np.arange(8, dtype=np.float32)
@@ -342,9 +436,22 @@ def _numpy_layer(cs, inp):
     bincount/cumsum/argsort dispatch, float64 matmuls, expit."""
     lg = inp["logits"].astype(np.float64)
     T, E, k, I = cs.T, cs.E, cs.k, cs.I
-    ids = np.argsort(-inp["logits"], axis=1, kind="stable")[:, :k]
-    p = scipy.special.softmax(lg, axis=1)
-    w = np.take_along_axis(p, ids, axis=1)
+    if cs.score_func == synth.SCORE_SIGMOID:
+        s = scipy.special.expit(lg)
+        key = s.astype(np.float32)
+        if inp.get("score_bias") is not None:
+            key = key + inp["score_bias"].astype(np.float32)   # float32 addition
+        ids = np.argsort(-key, axis=1, kind="stable")[:, :k]
+        w = np.take_along_axis(s, ids, axis=1)
+    else:
+        ids = np.argsort(-inp["logits"], axis=1, kind="stable")[:, :k]
+        p = scipy.special.softmax(lg, axis=1)
+        w = np.take_along_axis(p, ids, axis=1)
+        if cs.renormalize:
+            w = np.take_along_axis(np.exp(lg - lg.max(axis=1, keepdims=True)), ids, axis=1)
+    if cs.renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    w = w * cs.route_scale
     _, offsets, dst = _dispatch_by_sort(ids.astype(np.int64), E, cs.C)
     X = _widen(inp["x"])
     rnd = np.vectorize(oracle.round_bf16) if inp["x"].dtype == np.uint16 else (lambda a: a)
@@ -372,6 +479,8 @@ def _numpy_layer(cs, inp):
     ("decode_T8", dict(H=64, I=48, I_shared=40)),
     ("relu2_distinct_R8", dict(H=64, I=32)),
     ("skewed_bf16", dict(T=64, H=64, E=16, I=32, C=12)),
+    ("sigmoid_relu2_R16", dict(H=64, I=32)),
+    ("sigmoid_T2048", dict(T=24, H=64, E=8, I=32, C=20)),
 ])
 def test_forward_against_library_layer(name, over):
     cs = synth.case(name, **over)
