@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_T2048")
     ap.add_argument("--sweep", default="prefill_T256,prefill_T8192,decode_T1,decode_T32,"
-                    "relu2_distinct_R16,relu2_shared_R1",
+                    "relu2_distinct_R16,relu2_shared_R1,sigmoid_T2048",
                     help="comma-separated extra workloads timed briefly ('' = none)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
@@ -79,7 +79,9 @@ def run_workload(name, steps, warmup, with_events=True):
         cb = synth.replace(cs, seed=cs.seed + 1000 * b)
         banks.append((synth.make_x(cb, dev), synth.make_logits(cb, dev)))
     p = rde.make_problem(cs.T, cs.H, cs.E, cs.k, cs.I, cs.C, cs.n_shared, cs.I_shared,
-                         act_dtype=cs.act_fmt, w_dtype=cs.w_fmt, act=cs.act)
+                         act_dtype=cs.act_fmt, w_dtype=cs.w_fmt, act=cs.act,
+                         renormalize=cs.renormalize, score_func=cs.score_func,
+                         route_scale=cs.route_scale)
     n = rde.moe_workspace_bytes(p)
     ws = torch.empty(n, dtype=torch.uint8, device=dev)
     rde.moe_workspace_init(ws)
@@ -98,7 +100,7 @@ def run_workload(name, steps, warmup, with_events=True):
         meta = dict(offsets=offsets)
         if ev is not None:
             meta["stage_events"] = ev
-        rde.moe_forward(p, x, lg, None, None, base.w13, base.w2, base.s13, base.s2,
+        rde.moe_forward(p, x, lg, base.score_bias, None, None, base.w13, base.w2, base.s13, base.s2,
                         base.w13_sh, base.w2_sh, out, meta, ws)
 
     for i in range(warmup):
@@ -187,7 +189,7 @@ def cpu_baseline(res, n_tokens):
     w2 = oracle.from_torch(base.w2)
     conv = lambda t: None if t is None else oracle.from_torch(t)
     r = oracle.forward(sub, x, lg, w13, w2, conv(base.s13), conv(base.s2), conv(base.w13_sh),
-                       conv(base.w2_sh))
+                       conv(base.w2_sh), score_bias=conv(base.score_bias))
     sec = r["seconds"]
     return {"value": round(n_tokens / sec, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n_tokens} of {cs.T} tokens of {cs.name}: routing, count-first "

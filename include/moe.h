@@ -2,7 +2,8 @@
  * moe.h - C ABI of the MI355X (gfx950) Mixture-of-Experts layer forward.
  *
  * One MoE layer forward, in four steps:
- *   1. softmax top-k routing                              moe_route
+ *   1. softmax top-k routing, or sigmoid top-k routing    moe_route
+ *      with a selection-only correction bias
  *   2. count-first token dispatch: per-expert histogram,  moe_dispatch
  *      exclusive scan, stable scatter into expert-contiguous
  *      capacity buckets
@@ -17,7 +18,10 @@
  *     "Description": internal softmax routing or preselected FP32 expert
  *     ids/weights through k = 32, default SwiGLU experts and ReLU-square
  *     gate/down experts, isolation of malformed routes, BF16 store
- *     boundaries with FP32 final routing/reduction.
+ *     boundaries with FP32 final routing/reduction; and, in the commit
+ *     adding projected sigmoid routing, an FP32 selection-only correction
+ *     bias with mixture weights from the unbiased normalised scores, route
+ *     scaling kept.
  *   - afdEP count-first dispatch validation record ("change", "setup",
  *     fault list): count routes per expert first, compute prefix sums, then
  *     place each row at its known offset in an expert-contiguous buffer of
@@ -53,7 +57,8 @@
  * Layouts:
  *   x        [T, H]          act_dtype
  *   logits   [T, E]          float32
- *   ids      [T, k]          int32, slot 0 = largest logit
+ *   score_bias [E]           float32 correction bias of sigmoid routing
+ *   ids      [T, k]          int32, slot 0 = largest selection key
  *   w        [T, k]          float32 routing weights
  *   counts   [E]             int32 raw route count per expert (sum = T*k
  *                            minus malformed routes)
@@ -98,6 +103,9 @@ typedef int32_t moe_status;
 #define MOE_SWIGLU 0 /* h = silu(x W1^T) * (x W3^T), silu(a) = a / (1 + e^-a) */
 #define MOE_RELU2 1  /* h = max(x W1^T, 0)^2 */
 
+#define MOE_SOFTMAX 0 /* scores softmax(logits), selection on the logits */
+#define MOE_SIGMOID 1 /* scores sigmoid(logits), selection on score + bias */
+
 typedef struct moe_problem {
     int32_t T, H, E, k, I, C;
     int32_t n_shared;    /* always-on shared SwiGLU experts, weight 1 (0 = none) */
@@ -105,7 +113,9 @@ typedef struct moe_problem {
     int32_t act_dtype;   /* MOE_F32 or MOE_BF16: x, x_disp, y_disp, out */
     int32_t w_dtype;     /* MOE_F32 (needs act f32), MOE_BF16, MOE_E4M3 (needs act bf16) */
     int32_t act;         /* MOE_SWIGLU or MOE_RELU2 */
-    int32_t renormalize; /* 0: w = softmax over all E; 1: softmax over the k selected */
+    int32_t renormalize; /* 0: w = the selected scores; 1: normalised over the k selected */
+    int32_t score_func;  /* MOE_SOFTMAX or MOE_SIGMOID */
+    float route_scale;   /* every routed weight is multiplied by it; 0 means 1 */
 } moe_problem;
 
 /* Stage boundaries of moe_forward, for moe_meta.stage_events. */
@@ -144,18 +154,26 @@ moe_status moe_workspace_bytes(const moe_problem *p, size_t *bytes);
  * (by a fill kernel on `stream`). */
 moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
-/* Softmax top-k routing (PR 33963 "Measured CUDA kernel latency": internal
- * softmax routing).  Per token t, with m = max_e logits[t,e] and
- * S = sum_e exp(logits[t,e] - m):
- *   ids[t, 0..k-1] = the k experts with the largest logits, in descending
- *   logit order; equal logits (including -0 and +0) rank by lower index;
- *   NaN ranks below -inf.
- *   w[t, j] = exp(logits[t, ids[t,j]] - m) / S   (renormalize = 0), or the
- *   same numerators over their own sum (renormalize = 1).
- * Computed in float32.  A row of all -inf (or holding a NaN) gets NaN
- * weights. */
-moe_status moe_route(const moe_problem *p, const float *logits, int32_t *ids,
-                     float *w, void *ws, size_t ws_bytes, void *stream);
+/* Top-k routing (PR 33963 "Measured CUDA kernel latency": internal softmax
+ * routing; the commit adding projected sigmoid routing: FP32 selection-only
+ * correction bias, weights from the unbiased normalised scores, route
+ * scaling).  Per token t:
+ *   MOE_SOFTMAX: the selection key of expert e is logits[t,e]; its score is
+ *     exp(logits[t,e] - m) / S with m = max_e logits[t,e] and
+ *     S = sum_e exp(logits[t,e] - m).  score_bias must be NULL.
+ *   MOE_SIGMOID: the score is s_e = 1 / (1 + exp(-logits[t,e])), rounded
+ *     once to float32 (computed in double); the selection key is the float32
+ *     sum s_e + score_bias[e] (score_bias NULL: no bias).
+ *   ids[t, 0..k-1] = the k experts with the largest keys, in descending key
+ *   order; equal keys (including -0 and +0) rank by lower index; NaN ranks
+ *   below -inf.
+ *   w[t, j] = route_scale * score of ids[t,j] (renormalize = 0), or
+ *   route_scale * that score over the sum of the k selected scores
+ *   (renormalize = 1; for softmax the numerators exp(l - m) over their sum).
+ * Weights are computed in float32.  A softmax row of all -inf (or holding a
+ * NaN) gets NaN weights. */
+moe_status moe_route(const moe_problem *p, const float *logits, const float *score_bias,
+                     int32_t *ids, float *w, void *ws, size_t ws_bytes, void *stream);
 
 /* Count-first dispatch (afdEP count-first record: counts, prefix sums, rows
  * at known offsets).  ids may come from moe_route or be preselected by the
@@ -206,13 +224,14 @@ moe_status moe_combine(const moe_problem *p, const void *y_disp,
                        const float *y_shared, void *out, void *ws,
                        size_t ws_bytes, void *stream);
 
-/* The whole layer: route (or take ids_in / w_in when both are non-NULL),
+/* The whole layer: route as moe_route does with `logits` and `score_bias`
+ * (or take ids_in / w_in, unchanged, when both are non-NULL),
  * dispatch, expert FFN with the combine weights applied in the
  * down-projection epilogue, shared experts, and the final sum to token
  * order.  Same results as the separate calls: bit-identical metadata,
  * outputs within rounding of the separate path.  Intermediates live in ws. */
 moe_status moe_forward(const moe_problem *p, const void *x, const float *logits,
-                       const int32_t *ids_in, const float *w_in,
+                       const float *score_bias, const int32_t *ids_in, const float *w_in,
                        const void *w13, const void *w2, const float *s13,
                        const float *s2, const void *w13_sh, const void *w2_sh,
                        void *out, const moe_meta *meta, void *ws,

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "librde_moe.so")
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_SWIGLU, MOE_RELU2 = 0, 1
+MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 
 # every symbol the header declares
 EXPORTS = ("moe_workspace_bytes", "moe_workspace_init", "moe_route", "moe_dispatch",
@@ -28,7 +29,8 @@ EXPORTS = ("moe_workspace_bytes", "moe_workspace_init", "moe_route", "moe_dispat
 
 class moe_problem(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("T", "H", "E", "k", "I", "C", "n_shared", "I_shared",
-                                         "act_dtype", "w_dtype", "act", "renormalize")]
+                                         "act_dtype", "w_dtype", "act", "renormalize",
+                                         "score_func")] + [("route_scale", C.c_float)]
 
 
 MOE_N_STAGES = 8
@@ -63,12 +65,12 @@ def lib() -> C.CDLL:
         sig = {
             "moe_workspace_bytes": [pp, C.POINTER(C.c_size_t)],
             "moe_workspace_init": [P, S, P],
-            "moe_route": [pp, P, P, P, P, S, P],
+            "moe_route": [pp, P, P, P, P, P, S, P],
             "moe_dispatch": [pp, P, P, P, P, P, P, P, P, S, P],
             "moe_expert_ffn": [pp, P, P, P, P, P, P, P, P, S, P],
             "moe_shared_ffn": [pp, P, P, P, P, P, S, P],
             "moe_combine": [pp, P, P, P, P, P, P, S, P],
-            "moe_forward": [pp, P, P, P, P, P, P, P, P, P, P, P, C.POINTER(moe_meta), P, S, P],
+            "moe_forward": [pp, P, P, P, P, P, P, P, P, P, P, P, P, C.POINTER(moe_meta), P, S, P],
             "moe_error": [P, S, P, C.POINTER(i32)],
         }
         for name, args in sig.items():
@@ -89,9 +91,10 @@ def _status_string(s: int) -> str:
 
 
 def make_problem(T, H, E, k, I, C_cap, n_shared=0, I_shared=0, act_dtype=MOE_BF16,
-                 w_dtype=MOE_BF16, act=MOE_SWIGLU, renormalize=0) -> moe_problem:
+                 w_dtype=MOE_BF16, act=MOE_SWIGLU, renormalize=0, score_func=MOE_SOFTMAX,
+                 route_scale=1.0) -> moe_problem:
     return moe_problem(T, H, E, k, I, C_cap, n_shared, I_shared, act_dtype, w_dtype, act,
-                       renormalize)
+                       renormalize, score_func, route_scale)
 
 
 def _p(t) -> Optional[int]:
@@ -128,9 +131,9 @@ def moe_workspace_init(ws, stream=None):
     _check("moe_workspace_init", lib().moe_workspace_init(_p(ws), ws.numel(), _stream(stream)))
 
 
-def moe_route(p, logits, ids, w, ws, stream=None):
-    _check("moe_route", lib().moe_route(C.byref(p), _p(logits), _p(ids), _p(w), _p(ws),
-                                        ws.numel(), _stream(stream)))
+def moe_route(p, logits, score_bias, ids, w, ws, stream=None):
+    _check("moe_route", lib().moe_route(C.byref(p), _p(logits), _p(score_bias), _p(ids), _p(w),
+                                        _p(ws), ws.numel(), _stream(stream)))
 
 
 def moe_dispatch(p, x, ids, counts, offsets, row_src, route_dst, x_disp, ws, stream=None):
@@ -157,8 +160,8 @@ def moe_combine(p, y_disp, route_dst, w, y_shared, out, ws, stream=None):
                                             _stream(stream)))
 
 
-def moe_forward(p, x, logits, ids_in, w_in, w13, w2, s13, s2, w13_sh, w2_sh, out, meta, ws,
-                stream=None):
+def moe_forward(p, x, logits, score_bias, ids_in, w_in, w13, w2, s13, s2, w13_sh, w2_sh, out,
+                meta, ws, stream=None):
     """`meta` is None or a dict with any of ids, w, counts, offsets, row_src,
     route_dst (device tensors receiving the metadata) and stage_events (a
     list of MOE_N_STAGES torch.cuda.Event or None)."""
@@ -172,7 +175,8 @@ def moe_forward(p, x, logits, ids_in, w_in, w13, w2, s13, s2, w13_sh, w2_sh, out
             keep = (C.c_void_p * MOE_N_STAGES)(*[None if e is None else e.cuda_event for e in evs])
         m = moe_meta(*vals, C.cast(keep, C.c_void_p) if keep is not None else None)
     _check("moe_forward", lib().moe_forward(
-        C.byref(p), _p(x), _p(logits), _p(ids_in), _p(w_in), _p(w13), _p(w2), _p(s13), _p(s2),
+        C.byref(p), _p(x), _p(logits), _p(score_bias), _p(ids_in), _p(w_in), _p(w13), _p(w2),
+        _p(s13), _p(s2),
         _p(w13_sh), _p(w2_sh), _p(out), C.byref(m) if m is not None else None, _p(ws),
         ws.numel(), _stream(stream)))
 

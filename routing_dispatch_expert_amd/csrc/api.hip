@@ -43,6 +43,7 @@ inline int64_t r_max_of(const moe_problem& p) {
     const int64_t a = (int64_t)p.T * p.k, b = (int64_t)p.E * p.C;
     return a < b ? a : b;
 }
+inline float route_scale_of(const moe_problem& p) { return p.route_scale == 0.0f ? 1.0f : p.route_scale; }
 inline int act_bytes(const moe_problem& p) { return p.act_dtype == MOE_F32 ? 4 : 2; }
 inline int gemm_bm(const moe_problem& p) { return p.act_dtype == MOE_F32 ? kGemmF32BM : kGemmBM; }
 
@@ -56,6 +57,8 @@ moe_status check_problem(const moe_problem* pp) {
     if ((p.w_dtype == MOE_F32) != (p.act_dtype == MOE_F32)) return MOE_ERR_ARG;
     if (p.act != MOE_SWIGLU && p.act != MOE_RELU2) return MOE_ERR_ARG;
     if (p.renormalize != 0 && p.renormalize != 1) return MOE_ERR_ARG;
+    if (p.score_func != MOE_SOFTMAX && p.score_func != MOE_SIGMOID) return MOE_ERR_ARG;
+    if (!(p.route_scale >= 0.0f) || p.route_scale == INFINITY) return MOE_ERR_ARG;
     if (p.n_shared < 0 || p.n_shared > 8) return MOE_ERR_ARG;
     if (p.n_shared > 0 && p.I_shared <= 0) return MOE_ERR_ARG;
     if (p.E > 1024) return MOE_ERR_UNSUPPORTED;
@@ -417,15 +420,17 @@ moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
     return hip_status(launch_fill_i32((int32_t*)ws, CTRL_WORDS, 0, (hipStream_t)stream));
 }
 
-moe_status moe_route(const moe_problem* p, const float* logits, int32_t* ids, float* w, void* ws,
-                     size_t ws_bytes, void* stream) {
+moe_status moe_route(const moe_problem* p, const float* logits, const float* score_bias,
+                     int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream) {
     moe_status st = check_problem(p);
     if (st != MOE_OK) return st;
+    if (score_bias && p->score_func != MOE_SIGMOID) return MOE_ERR_ARG;
     Layout L;
     if ((st = check_ws(*p, ws, ws_bytes, &L)) != MOE_OK) return st;
     if (p->T == 0) return MOE_OK;
     if (!logits || !ids || !w) return MOE_ERR_ARG;
-    return hip_status(launch_route(logits, p->T, p->E, p->k, p->renormalize, ids, w, (hipStream_t)stream));
+    return hip_status(launch_route(logits, score_bias, p->T, p->E, p->k, p->score_func, p->renormalize,
+                                   route_scale_of(*p), ids, w, (hipStream_t)stream));
 }
 
 moe_status moe_dispatch(const moe_problem* p, const void* x, const int32_t* ids, int32_t* counts,
@@ -507,12 +512,13 @@ moe_status moe_combine(const moe_problem* p, const void* y_disp, const int32_t* 
                                      p->act_dtype, (hipStream_t)stream));
 }
 
-moe_status moe_forward(const moe_problem* p, const void* x, const float* logits, const int32_t* ids_in,
-                       const float* w_in, const void* w13, const void* w2, const float* s13,
+moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
+                       const float* score_bias, const int32_t* ids_in, const float* w_in, const void* w13, const void* w2, const float* s13,
                        const float* s2, const void* w13_sh, const void* w2_sh, void* out,
                        const moe_meta* meta, void* ws, size_t ws_bytes, void* stream) {
     moe_status st = check_problem(p);
     if (st != MOE_OK) return st;
+    if (score_bias && p->score_func != MOE_SIGMOID) return MOE_ERR_ARG;
     Layout L;
     if ((st = check_ws(*p, ws, ws_bytes, &L)) != MOE_OK) return st;
     const moe_problem& P = *p;
@@ -541,7 +547,8 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
         if (e == hipSuccess && w != w_in && Q)
             e = hipMemcpyAsync(w, w_in, sizeof(float) * Q, hipMemcpyDeviceToDevice, s);
     } else if (e == hipSuccess && P.T > 0) {
-        e = launch_route(logits, P.T, P.E, P.k, P.renormalize, ids, w, s);
+        e = launch_route(logits, score_bias, P.T, P.E, P.k, P.score_func, P.renormalize,
+                         route_scale_of(P), ids, w, s);
     }
     if (e == hipSuccess) e = mark(m, MOE_STAGE_ROUTE, s);
     if (e != hipSuccess) return MOE_ERR_HIP;

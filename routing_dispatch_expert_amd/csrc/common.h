@@ -30,8 +30,9 @@ constexpr int kCountBlock = kWave * kCountWaves * kCountPerLane;   // 2048
 
 inline int count_blocks(int64_t Q) { return (int)((Q + kCountBlock - 1) / kCountBlock); }
 
-hipError_t launch_route(const float* logits, int T, int E, int k, int renorm,
-                        int32_t* ids, float* w, hipStream_t s);
+hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
+                        int score_func, int renorm, float scale, int32_t* ids, float* w,
+                        hipStream_t s);
 
 // ids -> rexp (validated expert or -2), lrank (rank inside its block),
 // partial (per-block counts, turned into per-block bases by the last block),

@@ -1,15 +1,23 @@
-// Softmax top-k router: one wavefront per token.
+// Top-k router: one wavefront per token.
 //
 // Operation (onnxruntime PR 33963 "Extend MoEPacked for Bolt ReLU-square
 // routing and BF16 IQ2 precision", "Measured CUDA kernel latency": internal
-// softmax routing; the fleet megakernel report's MOE_TOPK step: top-k as k
-// rounds of a wave-wide maximum over the 64 lanes).
+// softmax routing, and the commit adding projected sigmoid routing with an
+// FP32 selection-only correction bias; the fleet megakernel report's
+// MOE_TOPK step: top-k as k rounds of a wave-wide maximum over the 64 lanes).
 //
-// Each lane holds E/64 logits (lane l holds experts l, l+64, ...: coalesced
-// row loads).  The softmax max and sum are wave reductions.  Top-k is k rounds
-// of a wave arg-max over a 64-bit key (order-preserving image of the float32
-// logit) << 32 | ~expert, so a larger logit wins and equal logits resolve to
-// the lower expert index; -0 is folded onto +0 and NaN maps to the lowest key.
+// Each lane holds E/64 experts (lane l holds experts l, l+64, ...: coalesced
+// row loads).  Top-k is k rounds of a wave arg-max over a 64-bit key
+// (order-preserving image of the float32 selection key) << 32 | ~expert, so a
+// larger key wins and equal keys resolve to the lower expert index; -0 is
+// folded onto +0 and NaN maps to the lowest key.
+//   softmax: key = logit; the softmax max and sum are wave reductions and a
+//            selected weight is recomputed from the key itself.
+//   sigmoid: score = sigma(logit) evaluated in double and rounded once to
+//            float32, key = score + bias in float32; the weight of a selected
+//            expert is its unbiased score, fetched from the owning lane.
+#include <type_traits>
+
 #include "common.h"
 
 namespace rde {
@@ -50,9 +58,11 @@ __device__ __forceinline__ float key_value(uint32_t o) {
     return (o & 0x80000000u) ? __uint_as_float(o & 0x7FFFFFFFu) : __uint_as_float(~o);
 }
 
-template <int EPL>
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
-                                                    int k, int renorm, int32_t* __restrict__ ids,
+template <int EPL, bool SIG>
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
+                                                    const float* __restrict__ bias, int T, int E,
+                                                    int k, int renorm, float scale,
+                                                    int32_t* __restrict__ ids,
                                                     float* __restrict__ w) {
     const int lane = threadIdx.x & (kWave - 1);
     const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
@@ -65,15 +75,24 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + kWave * i;
         v[i] = e < E ? row[e] : -INFINITY;
-        if (e < E) m = fmaxf(m, v[i]);  // fmaxf skips NaN
-        key[i] = e < E ? (((uint64_t)order_key(v[i]) << 32) | (uint32_t)(~e)) : 0ull;
+        float kf = v[i];
+        if (SIG) {
+            // sigma in double, one rounding to float32; the key adds the bias in float32
+            v[i] = (float)(1.0 / (1.0 + exp(-(double)v[i])));
+            kf = (bias != nullptr && e < E) ? v[i] + bias[e] : v[i];
+        } else if (e < E) {
+            m = fmaxf(m, v[i]);  // fmaxf skips NaN
+        }
+        key[i] = e < E ? (((uint64_t)order_key(kf) << 32) | (uint32_t)(~e)) : 0ull;
     }
-    m = wave_max(m);
     float s = 0.0f;
+    if (!SIG) {
+        m = wave_max(m);
 #pragma unroll
-    for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E) s += expf(v[i] - m);
-    s = wave_sum(s);
+        for (int i = 0; i < EPL; ++i)
+            if (lane + kWave * i < E) s += expf(v[i] - m);
+        s = wave_sum(s);
+    }
 
     int my_id = 0;
     float my_num = 0.0f, ssel = 0.0f;
@@ -86,7 +105,17 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
         for (int i = 0; i < EPL; ++i)
             if (key[i] == best) key[i] = 0ull;  // taken: keys are unique
         const int e = (int)(~(uint32_t)best);
-        const float num = expf(key_value((uint32_t)(best >> 32)) - m);
+        float num;
+        if (SIG) {
+            // the score of expert e lives in lane e % 64, slot e / 64
+            float mine = v[0];
+#pragma unroll
+            for (int i = 1; i < EPL; ++i)
+                if (i == (e >> 6)) mine = v[i];
+            num = __shfl(mine, e & (kWave - 1), kWave);
+        } else {
+            num = expf(key_value((uint32_t)(best >> 32)) - m);
+        }
         ssel += num;
         if (lane == j) {
             my_id = e;
@@ -95,22 +124,33 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     }
     if (lane < k) {
         ids[(int64_t)t * k + lane] = my_id;
-        w[(int64_t)t * k + lane] = my_num / (renorm ? ssel : s);
+        const float den = renorm ? ssel : (SIG ? 1.0f : s);
+        w[(int64_t)t * k + lane] = my_num / den * scale;
     }
 }
 
 }  // namespace
 
-hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
-                        float* w, hipStream_t s) {
+hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
+                        int score_func, int renorm, float scale, int32_t* ids, float* w,
+                        hipStream_t s) {
     if (T == 0) return hipSuccess;
     const int waves = 4;
     dim3 grid((T + waves - 1) / waves), block(waves * kWave);
-    if (E <= 64) hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, s, logits, T, E, k, renorm, ids, w);
-    else if (E <= 128) hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, s, logits, T, E, k, renorm, ids, w);
-    else if (E <= 256) hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, s, logits, T, E, k, renorm, ids, w);
-    else if (E <= 512) hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, s, logits, T, E, k, renorm, ids, w);
-    else hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, s, logits, T, E, k, renorm, ids, w);
+    auto go = [&](auto epl) {
+        constexpr int EPL = decltype(epl)::value;
+        if (score_func == MOE_SIGMOID)
+            hipLaunchKernelGGL((route_kernel<EPL, true>), grid, block, 0, s, logits, bias, T, E, k,
+                               renorm, scale, ids, w);
+        else
+            hipLaunchKernelGGL((route_kernel<EPL, false>), grid, block, 0, s, logits, bias, T, E,
+                               k, renorm, scale, ids, w);
+    };
+    if (E <= 64) go(std::integral_constant<int, 1>{});
+    else if (E <= 128) go(std::integral_constant<int, 2>{});
+    else if (E <= 256) go(std::integral_constant<int, 4>{});
+    else if (E <= 512) go(std::integral_constant<int, 8>{});
+    else go(std::integral_constant<int, 16>{});
     return hipGetLastError();
 }
 

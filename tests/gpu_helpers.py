@@ -22,7 +22,8 @@ DEV = "cuda:0"
 def problem(cs: synth.Case) -> rde.moe_problem:
     return rde.make_problem(cs.T, cs.H, cs.E, cs.k, cs.I, cs.C, cs.n_shared, cs.I_shared,
                             act_dtype=cs.act_fmt, w_dtype=cs.w_fmt, act=cs.act,
-                            renormalize=cs.renormalize)
+                            renormalize=cs.renormalize, score_func=cs.score_func,
+                            route_scale=cs.route_scale)
 
 
 def workspace(p) -> torch.Tensor:

@@ -61,6 +61,9 @@ def test_workspace_bytes_valid_and_monotone():
     (dict(act_dtype=7), rde.MOE_ERR_ARG), (dict(w_dtype=rde.MOE_BF16), rde.MOE_ERR_ARG),
     (dict(act_dtype=rde.MOE_BF16, w_dtype=rde.MOE_F32), rde.MOE_ERR_ARG),
     (dict(act=5), rde.MOE_ERR_ARG), (dict(renormalize=2), rde.MOE_ERR_ARG),
+    (dict(score_func=2), rde.MOE_ERR_ARG), (dict(route_scale=-1.0), rde.MOE_ERR_ARG),
+    (dict(route_scale=float("inf")), rde.MOE_ERR_ARG),
+    (dict(route_scale=float("nan")), rde.MOE_ERR_ARG),
     (dict(n_shared=2, I_shared=0), rde.MOE_ERR_ARG),
     (dict(H=200), rde.MOE_ERR_UNSUPPORTED), (dict(I=100), rde.MOE_ERR_UNSUPPORTED),
     (dict(E=2000, k=2), rde.MOE_ERR_UNSUPPORTED),
@@ -72,18 +75,29 @@ def test_invalid_problems_rejected_on_host(kw, want):
     assert st == want
     # every entry point applies the same check before touching the device
     L = rde.lib()
-    assert L.moe_route(C.byref(p), None, None, None, None, 0, None) == want
+    assert L.moe_route(C.byref(p), None, None, None, None, None, 0, None) == want
     assert L.moe_dispatch(C.byref(p), *([None] * 8), 0, None) == want
-    assert L.moe_forward(C.byref(p), *([None] * 11), None, None, 0, None) == want
+    assert L.moe_forward(C.byref(p), *([None] * 12), None, None, 0, None) == want
+
+
+def test_score_bias_needs_sigmoid_routing():
+    p = _prob()
+    L = rde.lib()
+    assert L.moe_route(C.byref(p), 16, 16, 16, 16, None, 0, None) == rde.MOE_ERR_ARG
+    assert L.moe_forward(C.byref(p), 16, 16, 16, *([None] * 9), None, None, 0,
+                         None) == rde.MOE_ERR_ARG
+    ps = _prob(score_func=rde.MOE_SIGMOID)
+    # with sigmoid routing the bias is accepted; the missing workspace is what fails
+    assert L.moe_route(C.byref(ps), 16, 16, 16, 16, None, 0, None) == rde.MOE_ERR_WORKSPACE
 
 
 def test_workspace_checked_before_launch():
     p = _prob()
     L = rde.lib()
     st, need = _ws_bytes(p)
-    assert L.moe_route(C.byref(p), 16, 16, 16, None, need, None) == rde.MOE_ERR_WORKSPACE
-    assert L.moe_route(C.byref(p), 16, 16, 16, 4096 + 8, need, None) == rde.MOE_ERR_WORKSPACE
-    assert L.moe_route(C.byref(p), 16, 16, 16, 4096, need - 1, None) == rde.MOE_ERR_WORKSPACE
+    assert L.moe_route(C.byref(p), 16, None, 16, 16, None, need, None) == rde.MOE_ERR_WORKSPACE
+    assert L.moe_route(C.byref(p), 16, None, 16, 16, 4096 + 8, need, None) == rde.MOE_ERR_WORKSPACE
+    assert L.moe_route(C.byref(p), 16, None, 16, 16, 4096, need - 1, None) == rde.MOE_ERR_WORKSPACE
     assert L.moe_workspace_init(None, 1024, None) == rde.MOE_ERR_WORKSPACE
     assert L.moe_error(None, 1024, None, None) == rde.MOE_ERR_WORKSPACE
 

@@ -38,11 +38,15 @@ SMALL = {
     "decode_fp8": ("skewed_fp8", dict(T=16, H=256, E=32, k=4, I=256, C=16)),
     "decode_rows_over_32": ("skewed_bf16", dict(T=180, H=256, E=32, k=2, I=128, C=180)),
     "decode_shared_T64": ("decode_T32", dict(T=64, H=256, I=128, I_shared=256, C=64)),
+    # sigmoid routing with a selection-only bias, normalised and scaled weights
+    "sigmoid_relu2_small": ("sigmoid_relu2_R16", dict(H=256, I=256)),
+    "sigmoid_prefill_small": ("sigmoid_T2048", dict(T=300, H=256, E=16, k=4, I=256, C=300)),
 }
 # Full-size workloads.
 FULL = ["tiny_fp32", "prefill_T256", "prefill_T2048", "prefill_T8192", "decode_T1", "decode_T8",
         "decode_T32", "relu2_distinct_R1", "relu2_shared_R1", "relu2_distinct_R8",
-        "relu2_shared_R8", "relu2_distinct_R16", "relu2_shared_R16", "skewed_bf16", "skewed_fp8"]
+        "relu2_shared_R8", "relu2_distinct_R16", "relu2_shared_R16", "skewed_bf16", "skewed_fp8",
+        "sigmoid_relu2_R16", "sigmoid_T2048"]
 
 
 def _case(key):
@@ -58,19 +62,24 @@ def _say(*a):
 
 # ---- routing -----------------------------------------------------------------
 
-def _route_gpu(cs, logits_dev):
+def _route_gpu(cs, logits_dev, bias_dev=None):
     p = problem(cs)
     ws = workspace(p)
     ids = torch.empty((cs.T, cs.k), dtype=torch.int32, device=DEV)
     w = torch.empty((cs.T, cs.k), dtype=torch.float32, device=DEV)
-    rde.moe_route(p, logits_dev, ids, w, ws)
+    rde.moe_route(p, logits_dev, bias_dev, ids, w, ws)
     torch.cuda.synchronize()
     return ids, w
 
 
-def _check_route(cs, logits):
-    ids, w = _route_gpu(cs, logits.to(DEV))
-    oi, ow = oracle.route(logits.numpy(), cs.k, cs.renormalize)
+def _oracle_route(cs, logits, bias):
+    return oracle.route(logits, cs.k, cs.renormalize, cs.score_func,
+                        None if bias is None else oracle.from_torch(bias), cs.route_scale)
+
+
+def _check_route(cs, logits, bias=None):
+    ids, w = _route_gpu(cs, logits.to(DEV), None if bias is None else bias.to(DEV))
+    oi, ow = _oracle_route(cs, logits.numpy(), bias)
     np.testing.assert_array_equal(np_i32(ids), oi)
     assert_f32_close(w, ow, "w")
     return ids, w, oi, ow
@@ -80,7 +89,7 @@ def _check_route(cs, logits):
 def test_route(key):
     cs = _case(key)
     _say("route", key, cs.T, cs.E, cs.k)
-    _check_route(cs, synth.make_logits(cs))
+    _check_route(cs, synth.make_logits(cs), synth.make_score_bias(cs))
 
 
 def test_route_pm16_bit_exact():
@@ -106,6 +115,27 @@ def test_route_ties_and_special_values(E, k):
     oi, ow = oracle.route(lg.numpy(), k)
     np.testing.assert_array_equal(np_i32(ids), oi)
     assert_f32_close(w, ow, "w")
+
+
+@pytest.mark.parametrize("E,k", [(7, 3), (64, 6), (240, 9), (1024, 32)])
+def test_route_sigmoid_ties_and_special_values(E, k):
+    # large logits saturate the float32 score to 1.0 (ties decided by index),
+    # grid biases make score + bias exact ties too; NaN and +-inf included
+    _say("route sigmoid ties", E, k)
+    g = torch.Generator().manual_seed(100 + E)
+    pool = torch.tensor([-1.0, 0.0, 1.0, 2.5, 20.0, 35.0, -40.0, float("inf"), float("-inf"),
+                         float("nan")])
+    T = 300
+    lg = pool[torch.randint(0, len(pool), (T, E), generator=g)]
+    lg[1] = torch.arange(E, dtype=torch.float32) / 8
+    bias = torch.randint(-8, 9, (E,), generator=g).to(torch.float32) / 32
+    for renorm, scale, b in ((0, 1.0, None), (1, 2.5, bias), (0, 0.75, bias)):
+        cs = synth.Case("sig_ties", T=T, H=128, E=E, k=k, I=128, C=T,
+                        score_func=synth.SCORE_SIGMOID, renormalize=renorm, route_scale=scale)
+        ids, w = _route_gpu(cs, lg.to(DEV), None if b is None else b.to(DEV))
+        oi, ow = _oracle_route(cs, lg.numpy(), b)
+        np.testing.assert_array_equal(np_i32(ids), oi)
+        assert_f32_close(w, ow, "w")
 
 
 # ---- dispatch ----------------------------------------------------------------
@@ -265,7 +295,8 @@ def _forward_gpu(cs, inp_dev, ids_in=None, w_in=None, with_meta=True):
                     offsets=torch.empty(cs.E + 1, dtype=torch.int32, device=DEV),
                     row_src=torch.empty(max(R, 1), dtype=torch.int32, device=DEV),
                     route_dst=torch.empty((cs.T, cs.k), dtype=torch.int32, device=DEV))
-    rde.moe_forward(p, inp_dev.x, inp_dev.logits, ids_in, w_in, inp_dev.w13, inp_dev.w2,
+    rde.moe_forward(p, inp_dev.x, inp_dev.logits, inp_dev.score_bias, ids_in, w_in,
+                    inp_dev.w13, inp_dev.w2,
                     inp_dev.s13, inp_dev.s2, inp_dev.w13_sh, inp_dev.w2_sh, out, meta, ws)
     n_bad = rde.moe_error(ws)
     return out, meta, n_bad
@@ -298,7 +329,7 @@ def test_forward_full_size(key):
     inp_dev = synth.make_inputs(cs, DEV)
     out, meta, _ = _forward_gpu(cs, inp_dev)
     logits = oracle.from_torch(inp_dev.logits)
-    ids, w = oracle.route(logits, cs.k, cs.renormalize)
+    ids, w = _oracle_route(cs, logits, inp_dev.score_bias)
     d = oracle.dispatch(ids, cs.E, cs.C)
     r = dict(ids=ids, w=w, **d)
     _check_meta(cs, meta, r)
@@ -325,7 +356,7 @@ def test_forward_preselected_is_bitwise_internal():
     # the same routes given as preselected ids / weights give bitwise the
     # same layer output (PR 33963: all outputs bitwise equal across the two
     # routing modes on identical routes)
-    for key in ("relu2_distinct_R16", "multi_tile_swiglu", "tiny_fp32"):
+    for key in ("relu2_distinct_R16", "multi_tile_swiglu", "tiny_fp32", "sigmoid_relu2_small"):
         cs = _case(key)
         _say("preselected bitwise", key)
         inp_dev = synth.make_inputs(cs, DEV)
@@ -379,14 +410,15 @@ def test_forward_empty_batch():
     zl = torch.empty((0, cs.E), dtype=torch.float32, device=DEV)
     w13 = torch.zeros((cs.E, 2 * cs.I, cs.H), dtype=torch.bfloat16, device=DEV)
     w2 = torch.zeros((cs.E, cs.H, cs.I), dtype=torch.bfloat16, device=DEV)
-    rde.moe_forward(p, z, zl, None, None, w13, w2, None, None, None, None, z,
+    rde.moe_forward(p, z, zl, None, None, None, w13, w2, None, None, None, None, z,
                     dict(counts=counts, offsets=offsets), ws)
     torch.cuda.synchronize()
     assert counts.sum().item() == 0 and offsets.sum().item() == 0
 
 
 def test_forward_matches_separate_entry_points():
-    for key in ("decode_shared_small", "ragged_skew_capacity", "tiny_fp32"):
+    for key in ("decode_shared_small", "ragged_skew_capacity", "tiny_fp32",
+                "sigmoid_prefill_small"):
         cs = _case(key)
         _say("forward vs separate", key)
         inp_dev = synth.make_inputs(cs, DEV)
@@ -396,7 +428,7 @@ def test_forward_matches_separate_entry_points():
         R = r_max(cs)
         ids = torch.empty((cs.T, cs.k), dtype=torch.int32, device=DEV)
         w = torch.empty((cs.T, cs.k), dtype=torch.float32, device=DEV)
-        rde.moe_route(p, inp_dev.logits, ids, w, ws)
+        rde.moe_route(p, inp_dev.logits, inp_dev.score_bias, ids, w, ws)
         counts = torch.empty(cs.E, dtype=torch.int32, device=DEV)
         offsets = torch.empty(cs.E + 1, dtype=torch.int32, device=DEV)
         row_src = torch.empty(max(R, 1), dtype=torch.int32, device=DEV)
