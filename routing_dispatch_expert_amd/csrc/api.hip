@@ -532,8 +532,12 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
     }
     moe_meta m = {};
     if (meta) m = *meta;
-    int32_t* ids = m.ids ? m.ids : at<int32_t>(ws, L.ids);
-    float* w = m.w ? m.w : at<float>(ws, L.w);
+    // router outputs; preselected routes are read in place unless the caller
+    // asked for a copy in its metadata outputs
+    int32_t* ids_out = m.ids ? m.ids : at<int32_t>(ws, L.ids);
+    float* w_out = m.w ? m.w : at<float>(ws, L.w);
+    const int32_t* ids = (pre && !m.ids) ? ids_in : ids_out;
+    const float* w = (pre && !m.w) ? w_in : w_out;
     int32_t* counts = m.counts ? m.counts : at<int32_t>(ws, L.counts);
     int32_t* offsets = m.offsets ? m.offsets : at<int32_t>(ws, L.offsets);
     int32_t* row_src = m.row_src ? m.row_src : at<int32_t>(ws, L.row_src);
@@ -542,13 +546,12 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
     const int64_t Q = (int64_t)P.T * P.k;
     hipError_t e = mark(m, MOE_STAGE_BEGIN, s);
     if (e == hipSuccess && pre) {
-        // preselected routes: copy into the metadata outputs when they differ
-        if (ids != ids_in && Q) e = hipMemcpyAsync(ids, ids_in, sizeof(int32_t) * Q, hipMemcpyDeviceToDevice, s);
-        if (e == hipSuccess && w != w_in && Q)
-            e = hipMemcpyAsync(w, w_in, sizeof(float) * Q, hipMemcpyDeviceToDevice, s);
+        // preselected routes: copied only into metadata outputs the caller gave
+        if (m.ids && m.ids != ids_in) e = launch_copy_u32(m.ids, ids_in, Q, s);
+        if (e == hipSuccess && m.w && m.w != w_in) e = launch_copy_u32(m.w, w_in, Q, s);
     } else if (e == hipSuccess && P.T > 0) {
         e = launch_route(logits, score_bias, P.T, P.E, P.k, P.score_func, P.renormalize,
-                         route_scale_of(P), ids, w, s);
+                         route_scale_of(P), ids_out, w_out, s);
     }
     if (e == hipSuccess) e = mark(m, MOE_STAGE_ROUTE, s);
     if (e != hipSuccess) return MOE_ERR_HIP;

@@ -136,6 +136,7 @@ hipError_t launch_combine(const void* y, int gather, const int32_t* route_dst, c
                           hipStream_t s);
 
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+hipError_t launch_copy_u32(void* dst, const void* src, int64_t n, hipStream_t s);
 
 int device_cu_count();
 

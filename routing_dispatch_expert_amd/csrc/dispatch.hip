@@ -19,6 +19,8 @@
 // base[block][e] + its in-block rank; a rank below C places the route at row
 // offsets[e] + rank.  The token's row is read once and stored to each of its
 // kept rows with 16-byte vector stores.
+#include <algorithm>
+
 #include "common.h"
 
 namespace rde {
@@ -234,7 +236,25 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
         p[i] = v;
 }
 
+// 32-bit word copy (preselected ids / weights into the caller's metadata
+// outputs): a kernel rather than a copy command, so a captured graph holds
+// kernel nodes only.
+__global__ void copy_u32_kernel(uint32_t* __restrict__ dst, const uint32_t* __restrict__ src,
+                                int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = src[i];
+}
+
 }  // namespace
+
+hipError_t launch_copy_u32(void* dst, const void* src, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(copy_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)dst,
+                       (const uint32_t*)src, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_count_rank(const int32_t* ids, int T, int k, int E, int C, int bm, int32_t* rexp,
                              int32_t* lrank, int32_t* partial, int32_t* counts, int32_t* offsets,

@@ -260,15 +260,19 @@ def make_inputs(cs: Case, device="cpu", experts: Optional[List[int]] = None) -> 
 
 
 def bad_routes(T: int, k: int, E: int, kind: str, seed: int = 0) -> torch.Tensor:
-    """Preselected int32 ids [T,k] with one malformed route class planted in
-    token 1 (the route classes of the count-first validation record:
-    negative, wide = out of range, duplicate within a token)."""
+    """Preselected int32 ids [T,k] (distinct experts per token) with one
+    malformed route of the count-first validation record's classes planted in
+    token 1: "dummy" = the index E of a dummy expert just past the real ones,
+    "negative" = -1, "wide" = the largest int32, "duplicate" = slot 1 repeats
+    slot 0; "none" plants nothing."""
     g = torch.Generator().manual_seed(seed)
     ids = torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(T)]).to(torch.int32)
-    if kind == "negative":
-        ids[1, 0] = -3
+    if kind == "dummy":
+        ids[1, k // 2] = E
+    elif kind == "negative":
+        ids[1, 0] = -1
     elif kind == "wide":
-        ids[1, k - 1] = E + 5
+        ids[1, k - 1] = 2 ** 31 - 1
     elif kind == "duplicate":
         if k < 2:
             raise ValueError("duplicate needs k >= 2")

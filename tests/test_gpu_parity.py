@@ -177,7 +177,7 @@ def test_dispatch(key):
     assert d["counts"].sum() == cs.T * cs.k
 
 
-@pytest.mark.parametrize("kind", ["negative", "wide", "duplicate"])
+@pytest.mark.parametrize("kind", ["dummy", "negative", "wide", "duplicate"])
 def test_dispatch_malformed_routes(kind):
     _say("dispatch malformed", kind)
     cs = synth.Case("bad", T=40, H=256, E=16, k=4, I=128, C=40)
@@ -382,7 +382,7 @@ def test_forward_deterministic_and_batch_invariant():
     assert torch.equal(c.view(torch.int16), a[sub].view(torch.int16))
 
 
-@pytest.mark.parametrize("kind", ["negative", "wide", "duplicate"])
+@pytest.mark.parametrize("kind", ["dummy", "negative", "wide", "duplicate"])
 def test_forward_malformed_routes_poison_only_their_token(kind):
     cs = synth.case("prefill_T256", T=24, H=256, E=16, k=4, I=128, C=24)
     _say("forward malformed", kind)
@@ -397,6 +397,117 @@ def test_forward_malformed_routes_poison_only_their_token(kind):
     o = out.float().cpu()
     assert torch.isnan(o[1]).all() and torch.isfinite(o[[0] + list(range(2, cs.T))]).all()
     assert_close(cs, out, r["out"], "out")
+
+
+# Shapes of the graph and preselected tests: rows per expert decide the path
+# (tiled grouped GEMM above 12 routes per expert on average, slot-indexed
+# expert GEMMs at or below it).
+GRAPH_SHAPES = {
+    "prefill": ("prefill_T256", dict(T=300, H=256, E=16, k=4, I=128, C=300)),
+    "decode": ("decode_T8", dict(H=256, I=128, I_shared=256)),
+}
+
+
+def _capture_forward(cs, inp_dev, ids_in, w_in, out, meta, p, ws):
+    """moe_forward captured into a graph on a side stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        rde.moe_forward(p, inp_dev.x, None if ids_in is not None else inp_dev.logits,
+                        None if ids_in is not None else inp_dev.score_bias, ids_in, w_in,
+                        inp_dev.w13, inp_dev.w2, inp_dev.s13, inp_dev.s2, inp_dev.w13_sh,
+                        inp_dev.w2_sh, out, meta, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    return g
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("shape", list(GRAPH_SHAPES))
+@pytest.mark.parametrize("kind", ["dummy", "negative", "wide", "duplicate"])
+def test_forward_malformed_routes_graph_replay(kind, shape):
+    # the graph execution of the count-first record's invalid-route runs:
+    # every replay poisons only the planted token and counts one bad route
+    name, over = GRAPH_SHAPES[shape]
+    cs = synth.case(name, **over)
+    _say("graph malformed", kind, shape)
+    inp_dev = synth.make_inputs(cs, DEV)
+    ids = synth.bad_routes(cs.T, cs.k, cs.E, kind).to(DEV)
+    w = torch.full((cs.T, cs.k), 1.0 / cs.k, device=DEV)
+    ref, meta_e, n_bad = _forward_gpu(cs, inp_dev, ids, w)
+    assert n_bad == 1
+    p = problem(cs)
+    ws = workspace(p)
+    out = torch.empty_like(ref)
+    route_dst = torch.empty((cs.T, cs.k), dtype=torch.int32, device=DEV)
+    g = _capture_forward(cs, inp_dev, ids, w, out, dict(route_dst=route_dst), p, ws)
+    for rep in range(3):
+        out.fill_(0)
+        route_dst.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(ref)), f"replay {rep}"
+        assert torch.equal(route_dst, meta_e["route_dst"])
+        assert rde.moe_error(ws) == 1
+        o = out.float().cpu()
+        assert torch.isnan(o[1]).all() and torch.isfinite(o[[0] + list(range(2, cs.T))]).all()
+
+
+@pytest.mark.parametrize("shape", list(GRAPH_SHAPES) + ["sigmoid"])
+def test_forward_graph_replay_matches_eager(shape):
+    # internal routing inside the graph; replays interleaved with eager work
+    name, over = GRAPH_SHAPES.get(shape, ("sigmoid_T2048", dict(T=300, H=256, E=16, k=4, I=128,
+                                                                C=300)))
+    cs = synth.case(name, **over)
+    _say("graph replay", shape)
+    inp_dev = synth.make_inputs(cs, DEV)
+    ref, meta_e, _ = _forward_gpu(cs, inp_dev)
+    p = problem(cs)
+    ws = workspace(p)
+    out = torch.empty_like(ref)
+    meta = {k: torch.empty_like(v) for k, v in meta_e.items()}
+    g = _capture_forward(cs, inp_dev, None, None, out, meta, p, ws)
+    for rep in range(3):
+        out.fill_(0)
+        for v in meta.values():
+            v.fill_(-5)
+        junk, _, _ = _forward_gpu(cs, inp_dev, with_meta=False)   # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(ref)), f"replay {rep}"
+        for key, v in meta.items():
+            assert torch.equal(_bits(v), _bits(meta_e[key])), (rep, key)
+    assert rde.moe_error(ws) == 0
+
+
+@pytest.mark.parametrize("shape", list(GRAPH_SHAPES))
+def test_forward_preselected_k32(shape):
+    # preselected float32 weights with k = 32 (the largest k), taken unchanged
+    name, over = GRAPH_SHAPES[shape]
+    over = dict(over, E=64, k=32, C=over.get("C", 8) * 32)
+    if shape == "decode":
+        over["T"] = 4
+        over["C"] = 4
+    cs = synth.case(name, **over)
+    _say("preselected k32", shape, cs.T)
+    inp_dev = synth.make_inputs(cs, DEV)
+    ids = synth.bad_routes(cs.T, cs.k, cs.E, "none", seed=32)
+    g = torch.Generator().manual_seed(33)
+    w = torch.rand((cs.T, cs.k), generator=g) * 0.1
+    out, meta, n_bad = _forward_gpu(cs, inp_dev, ids.to(DEV), w.to(DEV))
+    assert n_bad == 0
+    assert torch.equal(meta["ids"].cpu(), ids) and torch.equal(meta["w"].cpu(), w)
+    r = oracle.forward(cs, **oracle.inputs_numpy(inp_dev.to("cpu")), ids_in=ids.numpy(),
+                       w_in=w.double().numpy())
+    _check_meta(cs, meta, r)
+    assert_close(cs, out, r["out"], "out")
+    # without metadata outputs the routes are read in place: same bits
+    out2, _, _ = _forward_gpu(cs, inp_dev, ids.to(DEV), w.to(DEV), with_meta=False)
+    assert torch.equal(_bits(out2), _bits(out))
 
 
 def test_forward_empty_batch():

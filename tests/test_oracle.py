@@ -296,7 +296,7 @@ def test_capacity_drops_latest_routes_skewed():
         assert np.all(rd[qs[:16]] >= 0) and np.all(rd[qs[16:]] == -1)
 
 
-@pytest.mark.parametrize("kind", ["negative", "wide", "duplicate"])
+@pytest.mark.parametrize("kind", ["dummy", "negative", "wide", "duplicate"])
 def test_malformed_routes_are_isolated(kind):
     T, k, E = 6, 4, 16
     ids = synth.bad_routes(T, k, E, kind).numpy()
