@@ -13,8 +13,10 @@ timed region, the roofline of the dominant kernel, and the CPU oracle timed
 on a bounded sample of the same workload.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -139,6 +141,34 @@ def run_workload(name, steps, warmup, with_events=True):
                 bf=stage_bytes_flops(cs, R, touched, ab, wb), base=base)
 
 
+def kernel_source_sha256() -> str:
+    """sha256 over the library's kernel sources (file names and bytes, in
+    name order); a committed counter summary applies only while it matches."""
+    d = os.path.join(ROOT, "routing_dispatch_expert_amd", "csrc")
+    h = hashlib.sha256()
+    for n in sorted(os.listdir(d)):
+        if n.endswith((".hip", ".h")):
+            h.update(n.encode())
+            with open(os.path.join(d, n), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def counted_traffic(workload: str, stage: str):
+    """HBM bytes per launch of `stage` (FETCH_SIZE + WRITE_SIZE, each scaled by
+    a plain copy's reading) from the committed counter summary of `workload`;
+    None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"moe_forward_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        vals = dict(m.groups() for m in re.finditer(r"^([\w\[\]]+)=(\S+)$", f.read(), re.M))
+    if vals.get("source_sha256") != kernel_source_sha256() or vals.get("workload") != workload:
+        return None
+    v = vals.get(f"traffic_bytes[{stage}]")
+    return int(v) if v is not None else None
+
+
 def roofline_of(res, stage):
     us = res["stages"][stage]
     byts, flops = res["bf"][stage]
@@ -147,11 +177,13 @@ def roofline_of(res, stage):
     if t_mfma > t_hbm:
         ach = flops / (us * 1e-6) / 1e12
         return {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                "traffic": counted_traffic(res["cs"].name, stage),
                 "kernel": stage, "us": round(us, 2), "alg_flops": flops, "alg_bytes": byts}
     ach = byts / (us * 1e-6) / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": stage,
+            "frac": round(ach / HBM_PEAK_GBPS, 4),
+            "traffic": counted_traffic(res["cs"].name, stage), "kernel": stage,
             "us": round(us, 2), "alg_bytes": byts, "alg_flops": flops}
 
 
