@@ -250,13 +250,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         // wave-uniform LDS bases of this wave's DMA blocks in stage 0
         const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(sA[0]) + wave * 1024);
         const uint32_t lb0 = __builtin_amdgcn_readfirstlane(lds_addr(sB[0]) + wave * (FP8 ? 1024 : 2048));
-        // K order: the tile starts at k-tile `rot` and wraps.  Tiles running at
-        // the same time then read different column offsets of their rows, so
-        // rows with a power-of-two stride (weights and activations alike) do
-        // not all land on the same memory channels.  rot depends only on the
-        // expert and the n-tile, so a row's summation order never depends on
-        // the other tokens of the batch.
-        const int rot = (g * 7 + nt * 13) % nk;
+        // K order: the tile starts at k-tile `rot` and wraps.  Tiles of
+        // different experts running at the same time then read different
+        // column offsets of their rows, so weight rows with a power-of-two
+        // stride do not all land on the same memory channels.  The n-tiles of
+        // one expert share the rotation: they walk the expert's activation
+        // rows in the same order at about the same time, so those rows are
+        // fetched into L2 once and reused.  rot depends only on the expert, so
+        // a row's summation order never depends on the other tokens.
+        const int rot = (g * 13) % nk;
         // LA = A groups this wave loads (0, 1 or 2; wave-uniform)
         auto issue = [&](auto la_c, int kt) {
             constexpr int LA = decltype(la_c)::value;
