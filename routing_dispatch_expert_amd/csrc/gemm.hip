@@ -21,9 +21,12 @@
 // blocks, one workgroup per CU.  Operands go straight from global memory to
 // a 4-stage LDS ring (global_load_lds_dwordx4), three k-tiles in flight
 // while one is multiplied, one barrier per k-tile; rows of 64 bytes with an
-// XOR chunk swizzle keep the fragment reads free of bank conflicts.  Rows of
-// a tile past the end of its expert cost neither loads (16-row groups) nor
-// MFMAs (32-row blocks).
+// XOR chunk swizzle keep the fragment reads free of bank conflicts.  The ring
+// runs on across the tiles of a workgroup (the next tile's first k-tiles load
+// during the current tile's last ones).  Rows of a tile past the end of its
+// expert cost neither loads (16-row groups) nor MFMAs (32-row blocks).  bf16
+// results are regrouped in a small per-wave LDS patch so that stores write
+// 64 contiguous bytes per row.
 //
 // SwiGLU needs gate and up of the same output column in the same lane: the
 // B tile of a wave column holds 32 gate rows then the 32 matching up rows,
@@ -95,6 +98,7 @@ constexpr int kStages = 4;
 constexpr int A_STAGE = BM * BK * 2;          // bytes of one A stage (16 KB)
 constexpr int B_STAGE_BF16 = BN * BK * 2;     // 16 KB
 constexpr int B_STAGE_E4M3 = BN * BK;         // 8 KB
+constexpr int kOutPitch = 80;                 // bytes per row of a wave's 32 x 32 bf16 output patch
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 1 | (((r >> 2) & 1) << 1); }
 
@@ -123,24 +127,30 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
         : "memory");
 }
 
-// Wait until at most 2L / L / 0 of this thread's vector-memory operations are
-// outstanding (two, one or no later k-tiles still in flight, L = the thread's
-// DMA instructions per k-tile), then workgroup barrier.  No memory fence: LDS
-// written by global_load_lds is complete once the issuing thread's vmcnt has
-// dropped past it.
+// Wait until at most N of this thread's vector-memory operations are
+// outstanding, then workgroup barrier.  No memory fence: LDS written by
+// global_load_lds is complete once the issuing thread's vmcnt has dropped
+// past it.
 template <int N>
 __device__ __forceinline__ void waitcnt_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-template <int L>
-__device__ __forceinline__ void wait_tiles_barrier(int tiles_after) {
-    if (tiles_after >= 2) waitcnt_barrier<2 * L>();
-    else if (tiles_after == 1) waitcnt_barrier<L>();
-    else waitcnt_barrier<0>();
-}
-
-__device__ __forceinline__ void barrier_lds() {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// The same with a count known only at run time (0 .. 10).
+__device__ __forceinline__ void wait_barrier_dyn(int n) {
+    switch (n) {
+        case 0: waitcnt_barrier<0>(); break;
+        case 1: waitcnt_barrier<1>(); break;
+        case 2: waitcnt_barrier<2>(); break;
+        case 3: waitcnt_barrier<3>(); break;
+        case 4: waitcnt_barrier<4>(); break;
+        case 5: waitcnt_barrier<5>(); break;
+        case 6: waitcnt_barrier<6>(); break;
+        case 7: waitcnt_barrier<7>(); break;
+        case 8: waitcnt_barrier<8>(); break;
+        case 9: waitcnt_barrier<9>(); break;
+        case 10: waitcnt_barrier<10>(); break;
+        default: waitcnt_barrier<0>(); break;   // never smaller than needed
+    }
 }
 
 // 8 e4m3 codes (two dwords) -> bf16x8, exact.
@@ -162,6 +172,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char sA[kStages][A_STAGE];
     __shared__ __attribute__((aligned(1024))) unsigned char sB[kStages][B_STAGE];
     __shared__ int32_t s_mt[kMaxGroupsLds + 1];
+    __shared__ __attribute__((aligned(16))) unsigned char sOut[kThreads / 64][32 * kOutPitch];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -197,30 +208,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     // lane/2, 16-byte half lane%2 (one instruction per k-tile).
     const int dr = lane >> 2, ds = lane & 3;
 
-    for (int64_t Lt = vid; Lt < total; Lt += G) {
-        int g, cnt, ml, nt;
+    // wave-uniform LDS bases of this wave's DMA blocks in ring slot 0
+    const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(sA[0]) + wave * 1024);
+    const uint32_t lb0 = __builtin_amdgcn_readfirstlane(lds_addr(sB[0]) + wave * (FP8 ? 1024 : 2048));
+
+    // A tile's place in the problem and this thread's DMA sources (byte
+    // offsets at k = 0).  la = A groups this wave loads (0, 1 or 2).
+    struct Tile {
+        int g, nt, a_row0, rows, rot, la;
+        int64_t ga0, ga1, gb0, gb1;
+    };
+    auto make_tile = [&](int64_t Lt) {
+        Tile t;
+        int cnt, ml;
         if (uniform) {
-            g = (int)(Lt / ((int64_t)tiles_per_group * ntl));
-            const int loc = (int)(Lt - (int64_t)g * tiles_per_group * ntl);
+            t.g = (int)(Lt / ((int64_t)tiles_per_group * ntl));
+            const int loc = (int)(Lt - (int64_t)t.g * tiles_per_group * ntl);
             cnt = tiles_per_group;
-            nt = loc / cnt;
-            ml = loc - nt * cnt;
+            t.nt = loc / cnt;
+            ml = loc - t.nt * cnt;
+            t.a_row0 = ml * BM;
+            t.rows = min(BM, a.uniform_rows - t.a_row0);
         } else {
-            g = find_group(s_mt, a.n_groups, Lt, ntl);
-            cnt = s_mt[g + 1] - s_mt[g];
-            const int loc = (int)(Lt - (int64_t)s_mt[g] * ntl);
-            nt = loc / cnt;
-            ml = loc - nt * cnt;
+            t.g = find_group(s_mt, a.n_groups, Lt, ntl);
+            cnt = s_mt[t.g + 1] - s_mt[t.g];
+            const int loc = (int)(Lt - (int64_t)s_mt[t.g] * ntl);
+            t.nt = loc / cnt;
+            ml = loc - t.nt * cnt;
+            const int e0 = a.offsets[t.g], e1 = a.offsets[t.g + 1];
+            t.a_row0 = e0 + ml * BM;
+            t.rows = min(BM, e1 - t.a_row0);
         }
-        int a_row0, rows;
-        if (uniform) {
-            a_row0 = ml * BM;
-            rows = min(BM, a.uniform_rows - a_row0);
-        } else {
-            const int e0 = a.offsets[g], e1 = a.offsets[g + 1];
-            a_row0 = e0 + ml * BM;
-            rows = min(BM, e1 - a_row0);
-        }
+        const int g = t.g, nt = t.nt, rows = t.rows;
         auto brow_of = [&](int r) {
             if (EPI == EPI_SWIGLU) {
                 const int w2 = r >> 6, rr = r & 63;
@@ -228,28 +247,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
             }
             return min(nt * BN + r, a.N_w - 1);   // rows past N (ragged last tile): clamped
         };
-        // per-thread global byte offsets (k = 0) of its DMA sources
         const int ra0 = wave * 16 + dr, ra1 = ra0 + 128;
-        int64_t ar0 = a_row0 + min(ra0, rows - 1), ar1 = a_row0 + min(ra1, rows - 1);
+        int64_t ar0 = t.a_row0 + min(ra0, rows - 1), ar1 = t.a_row0 + min(ra1, rows - 1);
         if (a.gather) {  // expert rows read in place: the token of each route
             ar0 = a.row_src[ar0] / a.k_top;
             ar1 = a.row_src[ar1] / a.k_top;
         }
-        const int64_t ga0 = ar0 * a.lda * 2 + ((ds ^ swz(ra0)) * 16);
-        const int64_t ga1 = ar1 * a.lda * 2 + ((ds ^ swz(ra1)) * 16);
+        t.ga0 = ar0 * a.lda * 2 + ((ds ^ swz(ra0)) * 16);
+        t.ga1 = ar1 * a.lda * 2 + ((ds ^ swz(ra1)) * 16);
         const int64_t gbase = (int64_t)g * a.b_group_stride;
-        int64_t gb0, gb1 = 0;
+        t.gb1 = 0;
         if (FP8) {
             const int rb = wave * 32 + (lane >> 1), hb = lane & 1;
-            gb0 = (gbase + (int64_t)brow_of(rb) * a.k_seg) + ((hb ^ ((rb >> 2) & 1)) * 16);
+            t.gb0 = (gbase + (int64_t)brow_of(rb) * a.k_seg) + ((hb ^ ((rb >> 2) & 1)) * 16);
         } else {
             const int rb0 = wave * 32 + dr, rb1 = rb0 + 16;
-            gb0 = (gbase + (int64_t)brow_of(rb0) * a.k_seg) * 2 + ((ds ^ swz(rb0)) * 16);
-            gb1 = (gbase + (int64_t)brow_of(rb1) * a.k_seg) * 2 + ((ds ^ swz(rb1)) * 16);
+            t.gb0 = (gbase + (int64_t)brow_of(rb0) * a.k_seg) * 2 + ((ds ^ swz(rb0)) * 16);
+            t.gb1 = (gbase + (int64_t)brow_of(rb1) * a.k_seg) * 2 + ((ds ^ swz(rb1)) * 16);
         }
-        // wave-uniform LDS bases of this wave's DMA blocks in stage 0
-        const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(sA[0]) + wave * 1024);
-        const uint32_t lb0 = __builtin_amdgcn_readfirstlane(lds_addr(sB[0]) + wave * (FP8 ? 1024 : 2048));
         // K order: the tile starts at k-tile `rot` and wraps.  Tiles of
         // different experts running at the same time then read different
         // column offsets of their rows, so weight rows with a power-of-two
@@ -258,26 +273,48 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         // rows in the same order at about the same time, so those rows are
         // fetched into L2 once and reused.  rot depends only on the expert, so
         // a row's summation order never depends on the other tokens.
-        const int rot = (g * 13) % nk;
-        // LA = A groups this wave loads (0, 1 or 2; wave-uniform)
-        auto issue = [&](auto la_c, int kt) {
-            constexpr int LA = decltype(la_c)::value;
-            const int slot = kt % kStages;
-            int kr = kt + rot;
-            if (kr >= nk) kr -= nk;
-            const int k0 = kr * BK;
-            const int seg = k0 / a.k_seg;
-            const int64_t bo = (int64_t)seg * a.b_seg_stride + (k0 - seg * a.k_seg);
-            const uint32_t la = la0 + slot * A_STAGE, lb = lb0 + slot * B_STAGE;
-            if (LA >= 1) dma16(Ab + ga0 + (int64_t)k0 * 2, la);
-            if (LA >= 2) dma16(Ab + ga1 + (int64_t)k0 * 2, la + 8192);
-            if (FP8) {
-                dma16(Bb + gb0 + bo, lb);
-            } else {
-                dma16(Bb + gb0 + bo * 2, lb);
-                dma16(Bb + gb1 + bo * 2, lb + 1024);
-            }
-        };
+        t.rot = (g * 13) % nk;
+        t.la = __builtin_amdgcn_readfirstlane((16 * wave < rows) + (16 * (wave + 8) < rows));
+        return t;
+    };
+    // Load k-tile s (in the tile's own K order) of tile t into ring slot `slot`.
+    auto issue = [&](const Tile& t, int s, int slot) {
+        int kr = s + t.rot;
+        if (kr >= nk) kr -= nk;
+        const int k0 = kr * BK;
+        const int seg = k0 / a.k_seg;
+        const int64_t bo = (int64_t)seg * a.b_seg_stride + (k0 - seg * a.k_seg);
+        const uint32_t la = la0 + slot * A_STAGE, lb = lb0 + slot * B_STAGE;
+        if (t.la >= 1) dma16(Ab + t.ga0 + (int64_t)k0 * 2, la);
+        if (t.la >= 2) dma16(Ab + t.ga1 + (int64_t)k0 * 2, la + 8192);
+        if (FP8) {
+            dma16(Bb + t.gb0 + bo, lb);
+        } else {
+            dma16(Bb + t.gb0 + bo * 2, lb);
+            dma16(Bb + t.gb1 + bo * 2, lb + 1024);
+        }
+    };
+
+    // The load ring runs across tiles: while a tile's last kStages - 1
+    // k-tiles are multiplied, the next tile's first ones are loaded, so the
+    // pipeline never drains between tiles.  Ring slot of k-tile s of a tile =
+    // (sbase + s) % kStages, sbase = k-tiles of this workgroup's earlier tiles.
+    // Every wait bounds the number of this thread's DMA instructions issued
+    // after the awaited k-tile; other outstanding loads and stores (the
+    // next tile's row lookups, the epilogue's stores) only make it stricter.
+    int64_t Lt = vid;
+    if (Lt >= total) return;  // workgroup-uniform; nothing in flight
+    Tile cur = make_tile(Lt);
+    int sbase = 0;
+#pragma unroll
+    for (int st = 0; st < kStages - 1; ++st) issue(cur, st, st);   // nk >= 4
+
+    const int rA = lane & 31, half = lane >> 5;
+    for (; Lt < total; Lt += G) {
+        const bool has_next = Lt + G < total;
+        const Tile nxt = has_next ? make_tile(Lt + G) : cur;
+        const int cn = has_next ? LB + nxt.la : 0;   // next tile's DMA count per k-tile
+        const int g = cur.g, nt = cur.nt, a_row0 = cur.a_row0, rows = cur.rows;
 
         f32x16 acc[4][2];
 #pragma unroll
@@ -293,23 +330,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         const int n_act = __builtin_amdgcn_readfirstlane(
             col_ok ? max(0, min(4, (rows - 32 * wm + 63) / 64)) : 0);
 
-        barrier_lds();  // the previous tile's last stage is no longer read
-
-        const int rA = lane & 31, half = lane >> 5;
         // the pipelined k-loop, specialised on the number NA of active row
         // blocks of the wave's MFMAs and the number LA of A groups it loads
         auto kloop = [&](auto na_c, auto la_c) {
             constexpr int NA = decltype(na_c)::value;
             constexpr int LA = decltype(la_c)::value;
-#pragma unroll
-            for (int st = 0; st < kStages - 1; ++st)
-                if (st < nk) issue(la_c, st);
+            constexpr int LC = LB + LA;   // this tile's DMA count per k-tile
             for (int kt = 0; kt < nk; ++kt) {
-                wait_tiles_barrier<LB + LA>(min(kStages - 2, nk - 1 - kt));
-                if (kt + kStages - 1 < nk) issue(la_c, kt + kStages - 1);
+                // in flight behind k-tile kt: k-tiles kt + 1 and kt + 2, of this
+                // tile or (at the end) of the next one
+                if (kt + 2 < nk) waitcnt_barrier<2 * LC>();
+                else if (kt + 2 == nk) wait_barrier_dyn(LC + cn);
+                else wait_barrier_dyn(2 * cn);
+                const int s = kt + kStages - 1;
+                if (s < nk) issue(cur, s, (sbase + s) & (kStages - 1));
+                else if (has_next) issue(nxt, s - nk, (sbase + s) & (kStages - 1));
                 if (NA == 0) continue;
-                const unsigned char* sa = sA[kt % kStages];
-                const unsigned char* sb = sB[kt % kStages];
+                const int slot = (sbase + kt) & (kStages - 1);
+                const unsigned char* sa = sA[slot];
+                const unsigned char* sb = sB[slot];
 #pragma unroll
                 for (int ks = 0; ks < BK / 16; ++ks) {
                     const int c = ks * 2 + half;  // logical 16-byte chunk of this lane
@@ -338,10 +377,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
                 }
             }
         };
-        const int n_la = __builtin_amdgcn_readfirstlane((16 * wave < rows) + (16 * (wave + 8) < rows));
         auto by_la = [&](auto na_c) {
-            if (n_la == 2) kloop(na_c, std::integral_constant<int, 2>{});
-            else if (n_la == 1) kloop(na_c, std::integral_constant<int, 1>{});
+            if (cur.la == 2) kloop(na_c, std::integral_constant<int, 2>{});
+            else if (cur.la == 1) kloop(na_c, std::integral_constant<int, 1>{});
             else kloop(na_c, std::integral_constant<int, 0>{});
         };
         switch (n_act) {
@@ -353,42 +391,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         }
 
         // ---- epilogue: lane owns row (lane % 32) of each active row block and
-        // columns 8*i + 4*(lane/32) + 0..3 of each 32-column block ----
+        // columns 8*i + 4*(lane/32) + 0..3 of each 32-column block.  bf16
+        // results pass through the wave's own LDS patch, so that each store
+        // instruction writes 16 rows x 64 contiguous bytes instead of 16-byte
+        // pieces of 32 rows; float32 results are stored directly ----
         const int c4 = 4 * (lane >> 5);
+        unsigned char* so = sOut[wave];
+        const int sr = lane >> 2, sq = lane & 3;   // store phase: row (of 16), 16-byte chunk
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             if (mb >= n_act) continue;
-            const int row = (wm + 2 * mb) * 32 + (lane & 31);
-            if (row >= rows) continue;
-            const int64_t orow = (int64_t)a_row0 + row;
-            if (EPI == EPI_SWIGLU) {
-                const float* sc = FP8 ? a.bscale + (int64_t)g * a.N_w : nullptr;
-                __bf16* o = (__bf16*)a.out + orow * a.ldo + (int64_t)g * a.out_col_per_group;
+            const int rb = (wm + 2 * mb) * 32;
+            const int row = rb + (lane & 31);
+            // lanes past the expert's last row compute on a valid row and store nothing
+            const int64_t orow = (int64_t)a_row0 + min(row, rows - 1);
+            if (EPI == EPI_F32) {
+                if (row >= rows) continue;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int col = nt * 128 + wn * 32 + 8 * i + c4;
-                    float h[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float gv = acc[mb][0][4 * i + j], uv = acc[mb][1][4 * i + j];
-                        if (FP8) {
-                            gv *= sc[col + j];
-                            uv *= sc[a.I + col + j];
-                        }
-                        h[j] = silu_mul(gv, uv);
-                    }
-                    *(uint2*)(o + col) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-                }
-            } else {
-                float cw = 1.0f;
-                int64_t drow = orow;
-                if (EPI == EPI_COMBINE) {
-                    const int32_t q = a.row_src[orow];
-                    cw = a.route_w[q];
-                    drow = q;
-                }
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
+                for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int col = nt * BN + wn * 64 + nb * 32 + 8 * i + c4;
@@ -397,20 +417,62 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
                         for (int j = 0; j < 4; ++j) {
                             v[j] = acc[mb][nb][4 * i + j];
                             if (FP8) v[j] *= a.bscale[(int64_t)g * a.N_w + col + j];
+                        }
+                        *(float4*)((float*)a.out + orow * a.ldo + col) = make_float4(v[0], v[1], v[2], v[3]);
+                    }
+                continue;
+            }
+            float cw = 1.0f;
+            int32_t q = 0;
+            if (EPI == EPI_COMBINE) {
+                q = a.row_src[orow];
+                cw = a.route_w[q];
+            }
+            constexpr int NB = EPI == EPI_SWIGLU ? 1 : 2;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                // output columns of this 32-column block
+                const int col0 = EPI == EPI_SWIGLU ? nt * 128 + wn * 32 : nt * BN + wn * 64 + nb * 32;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int col = col0 + 8 * i + c4;
+                    float v[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (EPI == EPI_SWIGLU) {
+                            float gv = acc[mb][0][4 * i + j], uv = acc[mb][1][4 * i + j];
+                            if (FP8) {
+                                gv *= a.bscale[(int64_t)g * a.N_w + col + j];
+                                uv *= a.bscale[(int64_t)g * a.N_w + a.I + col + j];
+                            }
+                            v[j] = silu_mul(gv, uv);
+                        } else {
+                            v[j] = acc[mb][nb][4 * i + j];
+                            if (FP8) v[j] *= a.bscale[(int64_t)g * a.N_w + col + j];
                             if (EPI == EPI_RELU2) v[j] = v[j] > 0.0f ? v[j] * v[j] : 0.0f;
                             if (EPI == EPI_COMBINE) v[j] *= cw;
                         }
-                        if (EPI == EPI_F32) {
-                            *(float4*)((float*)a.out + drow * a.ldo + col) = make_float4(v[0], v[1], v[2], v[3]);
-                        } else {
-                            const int64_t oc = EPI == EPI_RELU2 ? (int64_t)g * a.out_col_per_group + col : col;
-                            *(uint2*)((__bf16*)a.out + drow * a.ldo + oc) =
-                                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                        }
                     }
+                    *(uint2*)(so + (lane & 31) * kOutPitch + (8 * i + c4) * 2) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
+                // the wave's LDS operations run in order: the reads below see
+                // the writes above, and the next block's writes follow them
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int r = sr + 16 * j;
+                    const uint4 u = *(const uint4*)(so + r * kOutPitch + sq * 16);
+                    int64_t drow = (int64_t)a_row0 + rb + r;
+                    if (EPI == EPI_COMBINE) drow = __shfl(q, r, kWave);
+                    const int64_t oc = (EPI == EPI_SWIGLU || EPI == EPI_RELU2)
+                                           ? (int64_t)g * a.out_col_per_group + col0 + sq * 8
+                                           : col0 + sq * 8;
+                    if (rb + r < rows) *(uint4*)((__bf16*)a.out + drow * a.ldo + oc) = u;
                 }
             }
         }
+        sbase += nk;
+        cur = nxt;
     }
 }
 
