@@ -32,7 +32,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_T2048")
     ap.add_argument("--sweep", default="prefill_T256,prefill_T8192,decode_T1,decode_T32,"
                     "relu2_distinct_R16,relu2_shared_R1,sigmoid_T2048",
@@ -278,7 +278,7 @@ def main():
     sweep = {}
     for name in [s for s in args.sweep.split(",") if s]:
         print(f"[bench] sweep {name}", file=sys.stderr, flush=True)
-        r2 = run_workload(name, max(5, args.steps // 3), 3)
+        r2 = run_workload(name, max(5, args.steps // 3), 10)
         ms2 = r2["wall"] / max(5, args.steps // 3) * 1e3
         sw = summary(r2)
         sw["tokens_per_s"] = round(r2["cs"].T / (ms2 * 1e-3), 1)
