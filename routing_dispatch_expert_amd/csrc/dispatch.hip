@@ -10,8 +10,8 @@
 // the number of lower lanes in its group, and the group's lowest lane adds
 // the group size.  Per-wave counts are then prefix-summed over the block's
 // waves (giving the rank of a route among the block's routes of its expert)
-// and the block totals are published.  The last block to arrive (atomic
-// ticket) turns the per-block totals into per-block bases, writes the raw
+// and the block totals are published (write-through stores).  The last
+// block to arrive (atomic ticket) turns the per-block totals into per-block bases, writes the raw
 // counts, the exclusive scan of min(count, C) and the m-tile table of the
 // grouped GEMM, and resets the ticket.
 //
@@ -83,29 +83,44 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int rank_w[kCountPerLane], ex[kCountPerLane];
     int n_bad = 0;
+    // all of this lane's ids first: one memory latency instead of one per step
 #pragma unroll
     for (int it = 0; it < kCountPerLane; ++it) {
         const int64_t q = q0 + it * kWave + lane;
-        int e = -1;
-        if (q < Q) {
-            e = ids[q];
-            bool ok = (e >= 0 && e < E);
-            const int64_t t = q / k;
-            const int j = (int)(q - t * k);
-            for (int jj = 0; ok && jj < j; ++jj) ok = (ids[t * k + jj] != e);
-            if (!ok) {
-                e = -2;
-                ++n_bad;
-            }
-            rexp[q] = e;
-        }
-        const bool valid = e >= 0;
-        uint64_t peers = __ballot(valid);
+        ex[it] = q < Q ? ids[q] : -1;
+    }
+#pragma unroll
+    for (int it = 0; it < kCountPerLane; ++it) {
+        const int64_t q = q0 + it * kWave + lane;
+        const bool inq = q < Q;
+        int e = ex[it];
+        const bool inrange = inq && e >= 0 && e < E;
+        // lanes of this 64-route step holding the same (in-range) expert
+        uint64_t peers = __ballot(inrange);
         for (int b = 0; b < ebits; ++b) {
-            const bool bit = valid && ((e >> b) & 1);
+            const bool bit = inrange && ((e >> b) & 1);
             const uint64_t m = __ballot(bit);
             peers &= bit ? m : ~m;
         }
+        // duplicate: an earlier slot of the same token holds the same expert.
+        // The token's slots are consecutive routes, so those in this step are
+        // the lanes just below; slots before the step (k not dividing the
+        // step) are read back from memory.
+        bool dup = false;
+        if (inrange) {
+            const int64_t t = q / k;
+            const int j = (int)(q - t * k);
+            const int first = lane - j;   // lane of the token's slot 0 (may be < 0)
+            dup = (peers & lt & ~((first > 0) ? (~0ull >> (64 - first)) : 0ull)) != 0;
+            for (int jj = 0; !dup && jj < -first; ++jj) dup = ids[t * k + jj] == e;
+        }
+        if (inq && (!inrange || dup)) {
+            e = -2;
+            ++n_bad;
+        }
+        if (inq) rexp[q] = e;
+        const bool valid = e >= 0;
+        peers &= ~__ballot(dup);  // the group of well-formed routes with this expert
         int r = 0;
         if (valid) {
             const int before = __popcll(peers & lt);
@@ -129,7 +144,9 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
             lds[w * E + e] = run;
             run += c;
         }
-        partial[(int64_t)blockIdx.x * E + e] = run;
+        // write-through to the device-coherent level: the last block reads it
+        __hip_atomic_store(&partial[(int64_t)blockIdx.x * E + e], run, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
 #pragma unroll
@@ -139,22 +156,39 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
     }
 
     // ---- last block: per-block bases, counts, offsets, m-tile table ----
-    __threadfence();
+    // Only the per-block totals cross blocks inside this kernel.  They were
+    // stored write-through (agent-scope atomic stores); once every thread's
+    // stores have completed the ticket is taken, and the last block reads
+    // them with agent-scope atomic loads.  No fence is needed, so the L2
+    // holds on to its dirty lines (an agent-scope fence writes back the
+    // whole L2 of the XCD).  Everything else this kernel writes is read by
+    // later kernels.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&ctrl[CTRL_TICKET], 1) == (int)gridDim.x - 1);
+    if (tid == 0)
+        s_last = (__hip_atomic_fetch_add(&ctrl[CTRL_TICKET], 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1);
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
     int32_t* kept = lds;
     int32_t* tiles = lds + E;
     const int nb = gridDim.x;
     for (int e = tid; e < E; e += blockDim.x) {
         int32_t run = 0;
-        for (int b = 0; b < nb; ++b) {
-            int32_t* p = &partial[(int64_t)b * E + e];
-            const int32_t c = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            *p = run;
-            run += c;
+        for (int b0 = 0; b0 < nb; b0 += 8) {
+            // eight blocks' totals in flight at once
+            int32_t c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                c[i] = b0 + i < nb ? __hip_atomic_load(&partial[(int64_t)(b0 + i) * E + e],
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                   : 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (b0 + i < nb) {
+                    partial[(int64_t)(b0 + i) * E + e] = run;
+                    run += c[i];
+                }
         }
         counts[e] = run;
         const int32_t kp = run < C ? run : C;

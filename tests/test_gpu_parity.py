@@ -186,6 +186,21 @@ def test_dispatch_malformed_routes(kind):
     assert d["n_bad"] == 1
 
 
+@pytest.mark.parametrize("k", [3, 9, 32])
+def test_dispatch_dense_malformed_routes(k):
+    # ids drawn with replacement from a small range plus out-of-range values:
+    # many duplicates inside tokens, including tokens whose slots straddle a
+    # 64-route step (k not dividing 64) and a 2048-route block
+    _say("dispatch dense malformed", k)
+    T, E = 700, 40
+    g = torch.Generator().manual_seed(k)
+    ids = torch.randint(-2, E + 2, (T, k), generator=g).to(torch.int32)
+    ids[::5] = torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(0, T, 5)]).to(torch.int32)
+    cs = synth.Case("dense_bad", T=T, H=128, E=E, k=k, I=128, C=T)
+    d = _check_dispatch(cs, synth.make_x(cs), ids.numpy())
+    assert 0 < d["n_bad"] < T * k
+
+
 def test_dispatch_ragged_blocks_and_max_k():
     # route counts around the 2048-route block boundary, k = 32, E = 1024
     for T, E, k, C in ((2049 // 8 + 1, 128, 8, 7), (64, 1024, 32, 3), (4097, 33, 1, 4097)):
