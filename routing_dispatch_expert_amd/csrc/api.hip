@@ -544,33 +544,44 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
     int32_t* route_dst = m.route_dst ? m.route_dst : at<int32_t>(ws, L.route_dst);
     hipStream_t s = (hipStream_t)stream;
     const int64_t Q = (int64_t)P.T * P.k;
+    const bool dec = decode_mode(P);
+    // bf16 layers read expert rows in place (no expert-contiguous copy of x)
+    const bool in_place = dec || P.act_dtype == MOE_BF16;
+    void* x_disp = at<void>(ws, L.x_disp);
+    int32_t* mt = at<int32_t>(ws, L.mt_off);
     hipError_t e = mark(m, MOE_STAGE_BEGIN, s);
     if (e == hipSuccess && pre) {
         // preselected routes: copied only into metadata outputs the caller gave
         if (m.ids && m.ids != ids_in) e = launch_copy_u32(m.ids, ids_in, Q, s);
         if (e == hipSuccess && m.w && m.w != w_in) e = launch_copy_u32(m.w, w_in, Q, s);
-    } else if (e == hipSuccess && P.T > 0) {
-        e = launch_route(logits, score_bias, P.T, P.E, P.k, P.score_func, P.renormalize,
-                         route_scale_of(P), ids_out, w_out, s);
     }
-    if (e == hipSuccess) e = mark(m, MOE_STAGE_ROUTE, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    void* x_disp = at<void>(ws, L.x_disp);
-    int32_t* mt = at<int32_t>(ws, L.mt_off);
-    e = launch_count_rank(ids, P.T, P.k, P.E, P.C, gemm_bm(P), at<int32_t>(ws, L.rexp),
-                          at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), counts, offsets, mt,
-                          at<int32_t>(ws, L.ctrl), s);
-    if (e == hipSuccess) e = mark(m, MOE_STAGE_COUNT, s);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    const bool dec = decode_mode(P);
-    // bf16 layers read expert rows in place (no expert-contiguous copy of x)
-    const bool in_place = dec || P.act_dtype == MOE_BF16;
-    if (P.T > 0)
-        e = launch_scatter(x, P.T, P.H, P.k, P.E, P.C, act_bytes(P), r_max_of(P), at<int32_t>(ws, L.rexp),
-                           at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), offsets, route_dst,
-                           row_src, in_place ? nullptr : x_disp, s);
-    if (e == hipSuccess) e = mark(m, MOE_STAGE_SCATTER, s);
-    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (in_place && P.T <= kSmallMaxT && P.E <= kSmallMaxE) {
+        // small batch: routing and the whole dispatch in one workgroup
+        e = launch_small_dispatch(pre ? nullptr : logits, score_bias, pre ? ids_in : nullptr, P.T,
+                                  P.k, P.E, P.C, gemm_bm(P), P.score_func, P.renormalize,
+                                  route_scale_of(P), ids_out, w_out, counts, offsets, mt, row_src,
+                                  r_max_of(P), route_dst, at<int32_t>(ws, L.ctrl), s);
+        for (int st = MOE_STAGE_ROUTE; e == hipSuccess && st <= MOE_STAGE_SCATTER; ++st) e = mark(m, st, s);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    } else {
+        if (!pre && P.T > 0)
+            e = launch_route(logits, score_bias, P.T, P.E, P.k, P.score_func, P.renormalize,
+                             route_scale_of(P), ids_out, w_out, s);
+        if (e == hipSuccess) e = mark(m, MOE_STAGE_ROUTE, s);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        e = launch_count_rank(ids, P.T, P.k, P.E, P.C, gemm_bm(P), at<int32_t>(ws, L.rexp),
+                              at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), counts, offsets, mt,
+                              at<int32_t>(ws, L.ctrl), s);
+        if (e == hipSuccess) e = mark(m, MOE_STAGE_COUNT, s);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        if (P.T > 0)
+            e = launch_scatter(x, P.T, P.H, P.k, P.E, P.C, act_bytes(P), r_max_of(P), at<int32_t>(ws, L.rexp),
+                               at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), offsets, route_dst,
+                               row_src, in_place ? nullptr : x_disp, s);
+        if (e == hipSuccess) e = mark(m, MOE_STAGE_SCATTER, s);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
     void* h = at<void>(ws, L.h);
     void* ybuf = at<void>(ws, L.ybuf);
     float* y_sh = P.n_shared ? at<float>(ws, L.y_shared) : nullptr;

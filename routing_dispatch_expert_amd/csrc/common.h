@@ -135,6 +135,15 @@ hipError_t launch_combine(const void* y, int gather, const int32_t* route_dst, c
                           const float* y_shared, void* out, int T, int k, int H, int act_dtype,
                           hipStream_t s);
 
+// Batches of at most kSmallMaxT tokens over at most kSmallMaxE experts: routing (or the caller's ids), ranks,
+// counts, offsets, m-tile table, row_src and route_dst in one workgroup.
+constexpr int kSmallMaxT = 64;
+constexpr int kSmallMaxE = 512;
+hipError_t launch_small_dispatch(const float* logits, const float* bias, const int32_t* ids_in,
+                                int T, int k, int E, int C, int bm, int score_func, int renorm,
+                                float scale, int32_t* ids, float* w, int32_t* counts,
+                                int32_t* offsets, int32_t* mt_off, int32_t* row_src, int64_t r_max,
+                                int32_t* route_dst, int32_t* ctrl, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 hipError_t launch_copy_u32(void* dst, const void* src, int64_t n, hipStream_t s);
 

@@ -20,8 +20,9 @@
 // offsets[e] + rank.  The token's row is read once and stored to each of its
 // kept rows with 16-byte vector stores.
 #include <algorithm>
+#include <type_traits>
 
-#include "common.h"
+#include "route_wave.h"
 
 namespace rde {
 namespace {
@@ -280,6 +281,178 @@ __global__ void copy_u32_kernel(uint32_t* __restrict__ dst, const uint32_t* __re
         dst[i] = src[i];
 }
 
+// ---- small batches: routing and the whole dispatch in one workgroup ---------
+// For T <= kSmallMaxT tokens (T*k <= 2048 routes) one 1024-thread workgroup
+// routes the tokens (or takes the caller's ids), ranks the routes, scans the
+// counts and places every route, so no block hand-off and no further launch is
+// needed.  Wave w ranks routes [128 w, 128 w + 128) in two 64-route steps,
+// exactly as the count kernel does; the ids live in LDS.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / kWave;        // 16
+constexpr int kSmallTokPerWave = kSmallMaxT / kSmallWaves;  // 4
+constexpr int kSmallSteps = 2;                            // 64-route steps per wave
+
+// Exclusive scan of one value per thread over the workgroup (1024 threads);
+// returns the thread's exclusive prefix and writes the total to *tot.
+__device__ int32_t block_exclusive_scan_1024(int32_t v, int32_t* s_wsum, int32_t* tot) {
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    int32_t x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) s_wsum[wv] = x;
+    __syncthreads();
+    if (wv == 0) {
+        int32_t u = lane < kSmallWaves ? s_wsum[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < kSmallWaves; off <<= 1) {
+            const int32_t y = __shfl_up(u, off, kWave);
+            if (lane >= off) u += y;
+        }
+        if (lane < kSmallWaves) s_wsum[lane] = u;   // inclusive over waves
+    }
+    __syncthreads();
+    const int32_t before = wv > 0 ? s_wsum[wv - 1] : 0;
+    *tot = s_wsum[kSmallWaves - 1];
+    __syncthreads();
+    return before + x - v;
+}
+
+template <int EPL, bool SIG>
+__global__ __launch_bounds__(kSmallThreads) void small_dispatch_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias,
+    const int32_t* __restrict__ ids_in, int T, int k, int E, int ebits, int C, int bm, int renorm,
+    float scale, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ mt_off,
+    int32_t* __restrict__ row_src, int64_t r_max, int32_t* __restrict__ route_dst,
+    int32_t* __restrict__ ctrl) {
+    extern __shared__ int32_t lds[];          // hist [kSmallWaves][E], then offsets [E + 1]
+    __shared__ int32_t s_ids[kSmallMaxT * 32];
+    __shared__ int32_t s_wsum[2][kSmallWaves];
+    __shared__ int32_t s_tot[2];
+    int32_t* hist = lds;
+    int32_t* s_off = lds + kSmallWaves * E;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const int Q = T * k;
+
+    // ---- routes ----
+    if (ids_in != nullptr) {
+        for (int q = tid; q < Q; q += kSmallThreads) s_ids[q] = ids_in[q];
+    } else {
+        float v[kSmallTokPerWave][EPL];
+#pragma unroll
+        for (int i = 0; i < kSmallTokPerWave; ++i) {   // all rows first: one memory latency
+            const int t = wv + kSmallWaves * i;
+            if (t < T) load_logits<EPL>(logits + (int64_t)t * E, E, lane, v[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kSmallTokPerWave; ++i) {
+            const int t = wv + kSmallWaves * i;
+            if (t >= T) break;  // wave-uniform
+            int id;
+            float wt;
+            route_row<EPL, SIG>(v[i], bias, E, k, renorm, scale, lane, id, wt);
+            if (lane < k) {
+                ids_out[t * k + lane] = id;
+                w_out[t * k + lane] = wt;
+                s_ids[t * k + lane] = id;
+            }
+        }
+    }
+    for (int i = tid; i < kSmallWaves * E; i += kSmallThreads) hist[i] = 0;
+    __syncthreads();
+
+    // ---- stable ranks within each wave's 128 routes (see count_rank_kernel) ----
+    int32_t* wh = hist + wv * E;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int rank_w[kSmallSteps], ex[kSmallSteps];
+    int n_bad = 0;
+#pragma unroll
+    for (int it = 0; it < kSmallSteps; ++it) {
+        const int q = wv * (kWave * kSmallSteps) + it * kWave + lane;
+        const bool inq = q < Q;
+        int e = inq ? s_ids[q] : -1;
+        const bool inrange = inq && e >= 0 && e < E;
+        uint64_t peers = __ballot(inrange);
+        for (int b = 0; b < ebits; ++b) {
+            const bool bit = inrange && ((e >> b) & 1);
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        bool dup = false;
+        if (inrange) {
+            const int t = q / k, j = q - t * k;
+            const int first = lane - j;
+            dup = (peers & lt & ~((first > 0) ? (~0ull >> (64 - first)) : 0ull)) != 0;
+            for (int jj = 0; !dup && jj < -first; ++jj) dup = s_ids[t * k + jj] == e;
+        }
+        if (inq && (!inrange || dup)) {
+            e = -2;
+            ++n_bad;
+        }
+        const bool valid = e >= 0;
+        peers &= ~__ballot(dup);
+        int r = 0;
+        if (valid) {
+            const int before = __popcll(peers & lt);
+            r = wh[e] + before;
+            if (before == 0) wh[e] += __popcll(peers);
+        }
+        rank_w[it] = r;
+        ex[it] = e;
+    }
+    int wave_bad = n_bad;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wave_bad += __shfl_xor(wave_bad, off, kWave);
+    if (wave_bad && lane == 0) atomicAdd(&ctrl[CTRL_BAD_ROUTES], wave_bad);
+    __syncthreads();
+
+    // ---- per-expert totals, wave bases, exclusive scans ----
+    int32_t kept = 0, tiles = 0;
+    for (int e = tid; e < E; e += kSmallThreads) {   // E <= 1024: one expert per thread
+        int32_t run = 0;
+        for (int w = 0; w < kSmallWaves; ++w) {
+            const int32_t c = hist[w * E + e];
+            hist[w * E + e] = run;
+            run += c;
+        }
+        counts[e] = run;
+        kept = run < C ? run : C;
+        tiles = (kept + bm - 1) / bm;
+    }
+    const int32_t off_e = block_exclusive_scan_1024(kept, s_wsum[0], &s_tot[0]);
+    const int32_t mt_e = block_exclusive_scan_1024(tiles, s_wsum[1], &s_tot[1]);
+    if (tid < E) {
+        offsets[tid] = off_e;
+        mt_off[tid] = mt_e;
+        s_off[tid] = off_e;
+    }
+    if (tid == 0) {
+        offsets[E] = s_tot[0];
+        mt_off[E] = s_tot[1];
+        s_off[E] = s_tot[0];
+    }
+    __syncthreads();
+
+    // ---- place every route ----
+#pragma unroll
+    for (int it = 0; it < kSmallSteps; ++it) {
+        const int q = wv * (kWave * kSmallSteps) + it * kWave + lane;
+        if (q >= Q) continue;
+        const int e = ex[it];
+        int32_t row = -2;
+        if (e >= 0) {
+            const int32_t r = hist[wv * E + e] + rank_w[it];
+            row = r < C ? s_off[e] + r : -1;
+            if (row >= 0) row_src[row] = q;
+        }
+        route_dst[q] = row;
+    }
+    for (int64_t r = s_off[E] + tid; r < r_max; r += kSmallThreads) row_src[r] = -1;
+}
+
 }  // namespace
 
 hipError_t launch_copy_u32(void* dst, const void* src, int64_t n, hipStream_t s) {
@@ -287,6 +460,33 @@ hipError_t launch_copy_u32(void* dst, const void* src, int64_t n, hipStream_t s)
     const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
     hipLaunchKernelGGL(copy_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)dst,
                        (const uint32_t*)src, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_small_dispatch(const float* logits, const float* bias, const int32_t* ids_in,
+                                int T, int k, int E, int C, int bm, int score_func, int renorm,
+                                float scale, int32_t* ids, float* w, int32_t* counts,
+                                int32_t* offsets, int32_t* mt_off, int32_t* row_src, int64_t r_max,
+                                int32_t* route_dst, int32_t* ctrl, hipStream_t s) {
+    int ebits = 0;
+    while ((1 << ebits) < E) ++ebits;
+    const size_t lds = sizeof(int32_t) * ((size_t)kSmallWaves * E + E + 1);
+    auto go = [&](auto epl) {
+        constexpr int EPL = decltype(epl)::value;
+        if (score_func == MOE_SIGMOID)
+            hipLaunchKernelGGL((small_dispatch_kernel<EPL, true>), dim3(1), dim3(kSmallThreads), lds, s,
+                               logits, bias, ids_in, T, k, E, ebits, C, bm, renorm, scale, ids, w,
+                               counts, offsets, mt_off, row_src, r_max, route_dst, ctrl);
+        else
+            hipLaunchKernelGGL((small_dispatch_kernel<EPL, false>), dim3(1), dim3(kSmallThreads), lds,
+                               s, logits, bias, ids_in, T, k, E, ebits, C, bm, renorm, scale, ids, w,
+                               counts, offsets, mt_off, row_src, r_max, route_dst, ctrl);
+    };
+    if (E <= 64) go(std::integral_constant<int, 1>{});
+    else if (E <= 128) go(std::integral_constant<int, 2>{});
+    else if (E <= 256) go(std::integral_constant<int, 4>{});
+    else if (E <= kSmallMaxE) go(std::integral_constant<int, 8>{});
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

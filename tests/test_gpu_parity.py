@@ -525,6 +525,25 @@ def test_forward_preselected_k32(shape):
     assert torch.equal(_bits(out2), _bits(out))
 
 
+@pytest.mark.parametrize("T,k", [(64, 9), (40, 32), (7, 3)])
+def test_forward_small_batch_dense_malformed(T, k):
+    # batches of at most 64 tokens are routed and dispatched by one workgroup:
+    # many duplicate / out-of-range ids, tokens straddling 64-route steps
+    cs = synth.case("prefill_T256", T=T, H=256, E=40, k=k, I=128, C=T)
+    _say("forward small dense malformed", T, k)
+    inp_dev = synth.make_inputs(cs, DEV)
+    g = torch.Generator().manual_seed(T * k)
+    ids = torch.randint(-1, cs.E + 1, (T, k), generator=g).to(torch.int32)
+    ids[::4] = torch.stack([torch.randperm(cs.E, generator=g)[:k] for _ in range(0, T, 4)]).to(torch.int32)
+    w = torch.rand((T, k), generator=g)
+    out, meta, n_bad = _forward_gpu(cs, inp_dev, ids.to(DEV), w.to(DEV))
+    r = oracle.forward(cs, **oracle.inputs_numpy(inp_dev.to("cpu")), ids_in=ids.numpy(),
+                       w_in=w.double().numpy())
+    assert n_bad == r["n_bad"] > 0
+    _check_meta(cs, meta, r)
+    assert_close(cs, out, r["out"], "out")
+
+
 def test_forward_empty_batch():
     cs = synth.case("prefill_T256", T=0, H=256, E=16, I=128)
     _say("forward empty")
