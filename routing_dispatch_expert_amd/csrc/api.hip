@@ -270,13 +270,16 @@ bool decode_mode(const moe_problem& p) {
 
 int decode_grid() { return device_cu_count(); }  // 4 wavefronts x 32 KB LDS ring per CU
 
+// mt: prefix over experts of ceil(rows / kDecodeBM) (the dispatch's m-tile
+// table built with that tile height).
 DecodeSeg routed_seg1(const moe_problem& p, const void* A, int gather, const int32_t* offsets,
-                      const void* w13, const float* s13, void* h) {
+                      const int32_t* mt, const void* w13, const float* s13, void* h) {
     DecodeSeg s = {};
     s.A = A;
     s.lda = p.H;
     s.gather = gather;
     s.offsets = offsets;
+    s.mt = mt;
     s.B = w13;
     s.N_w = p.act == MOE_SWIGLU ? 2 * p.I : p.I;
     s.b_group_stride = (int64_t)s.N_w * p.H;
@@ -292,12 +295,13 @@ DecodeSeg routed_seg1(const moe_problem& p, const void* A, int gather, const int
     return s;
 }
 
-DecodeSeg routed_seg2(const moe_problem& p, const void* h, const int32_t* offsets, const void* w2,
-                      const float* s2, int epi, void* out) {
+DecodeSeg routed_seg2(const moe_problem& p, const void* h, const int32_t* offsets, const int32_t* mt,
+                      const void* w2, const float* s2, int epi, void* out) {
     DecodeSeg s = {};
     s.A = h;
     s.lda = p.I;
     s.offsets = offsets;
+    s.mt = mt;
     s.B = w2;
     s.N_w = p.H;
     s.b_group_stride = (int64_t)p.H * p.I;
@@ -365,6 +369,9 @@ hipError_t run_decode(const DecodeSeg* a, const DecodeSeg* b, const int32_t* row
     d.row_src = row_src;
     d.k_top = k;
     d.route_w = route_w;
+    // a routed segment (tile table staged in LDS) can only be the first one
+    if (d.n_seg > 1 && d.seg[1].offsets) return hipErrorInvalidValue;
+    if (d.seg[0].offsets && (!d.seg[0].mt || d.seg[0].n_groups > kDecodeMaxGroups)) return hipErrorInvalidValue;
     // Split K over a workgroup's 4 wavefronts when the launch has fewer units
     // than the chip has wavefronts and each wavefront still gets >= 8 K groups
     // of 64 (a longer stream per wavefront keeps its ring full).  The number of
@@ -465,13 +472,14 @@ moe_status moe_expert_ffn(const moe_problem* p, const void* x_disp, const int32_
     if ((p->w_dtype == MOE_E4M3) != (s13 != nullptr && s2 != nullptr)) return MOE_ERR_ARG;
     hipStream_t s = (hipStream_t)stream;
     void* h = at<void>(ws, L.h);
+    int32_t* mt = at<int32_t>(ws, L.mt_off);
     if (decode_mode(*p)) {
-        const DecodeSeg g1 = routed_seg1(*p, x_disp, 0, offsets, w13, s13, h);
+        if (launch_tile_table(offsets, p->E, p->C, kDecodeBM, mt, s) != hipSuccess) return MOE_ERR_HIP;
+        const DecodeSeg g1 = routed_seg1(*p, x_disp, 0, offsets, mt, w13, s13, h);
         if (run_decode(&g1, nullptr, nullptr, p->k, nullptr, p->w_dtype, (int64_t)p->T * p->k, s) != hipSuccess) return MOE_ERR_HIP;
-        const DecodeSeg g2 = routed_seg2(*p, h, offsets, w2, s2, EPI_STORE, y_disp);
+        const DecodeSeg g2 = routed_seg2(*p, h, offsets, mt, w2, s2, EPI_STORE, y_disp);
         return hip_status(run_decode(&g2, nullptr, nullptr, p->k, nullptr, p->w_dtype, (int64_t)p->T * p->k, s));
     }
-    int32_t* mt = at<int32_t>(ws, L.mt_off);
     if (launch_tile_table(offsets, p->E, p->C, gemm_bm(*p), mt, s) != hipSuccess) return MOE_ERR_HIP;
     if (run_gemm1(*p, x_disp, offsets, mt, w13, s13, h, s) != hipSuccess) return MOE_ERR_HIP;
     return hip_status(run_gemm2(*p, h, offsets, mt, w2, s2, EPI_STORE, y_disp, nullptr, nullptr, s));
@@ -549,6 +557,9 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
     const bool in_place = dec || P.act_dtype == MOE_BF16;
     void* x_disp = at<void>(ws, L.x_disp);
     int32_t* mt = at<int32_t>(ws, L.mt_off);
+    // the m-tile table serves the grouped GEMM (its tile height) or the
+    // slot-indexed decode GEMMs (32-row work items)
+    const int tile_bm = dec ? kDecodeBM : gemm_bm(P);
     hipError_t e = mark(m, MOE_STAGE_BEGIN, s);
     if (e == hipSuccess && pre) {
         // preselected routes: copied only into metadata outputs the caller gave
@@ -559,7 +570,7 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
     if (in_place && P.T <= kSmallMaxT && P.E <= kSmallMaxE) {
         // small batch: routing and the whole dispatch in one workgroup
         e = launch_small_dispatch(pre ? nullptr : logits, score_bias, pre ? ids_in : nullptr, P.T,
-                                  P.k, P.E, P.C, gemm_bm(P), P.score_func, P.renormalize,
+                                  P.k, P.E, P.C, tile_bm, P.score_func, P.renormalize,
                                   route_scale_of(P), ids_out, w_out, counts, offsets, mt, row_src,
                                   r_max_of(P), route_dst, at<int32_t>(ws, L.ctrl), s);
         for (int st = MOE_STAGE_ROUTE; e == hipSuccess && st <= MOE_STAGE_SCATTER; ++st) e = mark(m, st, s);
@@ -570,7 +581,7 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
                              route_scale_of(P), ids_out, w_out, s);
         if (e == hipSuccess) e = mark(m, MOE_STAGE_ROUTE, s);
         if (e != hipSuccess) return MOE_ERR_HIP;
-        e = launch_count_rank(ids, P.T, P.k, P.E, P.C, gemm_bm(P), at<int32_t>(ws, L.rexp),
+        e = launch_count_rank(ids, P.T, P.k, P.E, P.C, tile_bm, at<int32_t>(ws, L.rexp),
                               at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), counts, offsets, mt,
                               at<int32_t>(ws, L.ctrl), s);
         if (e == hipSuccess) e = mark(m, MOE_STAGE_COUNT, s);
@@ -589,12 +600,12 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
     if (dec && P.T > 0) {
         // slot-indexed expert GEMMs; routed and shared units share each launch
         void* h_sh = at<void>(ws, L.h_sh);
-        const DecodeSeg r1 = routed_seg1(P, x, 1, offsets, w13, s13, h);
+        const DecodeSeg r1 = routed_seg1(P, x, 1, offsets, mt, w13, s13, h);
         const DecodeSeg sh1 = P.n_shared ? shared_seg1(P, x, w13_sh, h_sh) : DecodeSeg{};
         e = run_decode(&r1, P.n_shared ? &sh1 : nullptr, row_src, P.k, w, P.w_dtype, (int64_t)P.T * P.k, s);
         if (e == hipSuccess) e = mark(m, MOE_STAGE_GEMM1, s);
         if (e != hipSuccess) return MOE_ERR_HIP;
-        const DecodeSeg r2 = routed_seg2(P, h, offsets, w2, s2, EPI_COMBINE, ybuf);
+        const DecodeSeg r2 = routed_seg2(P, h, offsets, mt, w2, s2, EPI_COMBINE, ybuf);
         const DecodeSeg sh2 = P.n_shared ? shared_seg2(P, h_sh, w2_sh, y_sh) : DecodeSeg{};
         e = run_decode(&r2, P.n_shared ? &sh2 : nullptr, row_src, P.k, w, P.w_dtype, (int64_t)P.T * P.k, s);
         if (e == hipSuccess) e = mark(m, MOE_STAGE_GEMM2, s);

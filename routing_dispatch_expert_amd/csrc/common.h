@@ -99,11 +99,14 @@ hipError_t launch_gemm_f32(const GemmArgs& a, int grid, hipStream_t s);
 // row itself) or the shared experts (offsets == null: uniform_rows rows,
 // activation row = row).  blocks = units per group (16 output columns for
 // SwiGLU, 32 otherwise).
+constexpr int kDecodeBM = 32;        // activation rows per decode work item
+constexpr int kDecodeMaxGroups = 1024;
 struct DecodeSeg {
     const void* A;
     int64_t lda;
     int gather;
-    const int32_t* offsets;
+    const int32_t* offsets;     // routed: expert row ranges (and mt); uniform: NULL
+    const int32_t* mt;          // routed: prefix over experts of ceil(rows / kDecodeBM)
     int uniform_rows;
     const void* B;
     int64_t b_group_stride;

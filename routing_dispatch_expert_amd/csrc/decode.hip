@@ -69,6 +69,18 @@ __device__ __forceinline__ void wait_own(int stages_after) {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Expert owning tile ti: the largest g with tbl[g] <= ti (tbl non-decreasing,
+// tbl[0] = 0; experts without rows have tbl[g] == tbl[g + 1]).
+__device__ __forceinline__ int find_tile_group(const int32_t* tbl, int n_groups, int ti) {
+    int lo = 0, hi = n_groups - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tbl[mid] <= ti) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
 __device__ __forceinline__ int dswz(int r) { return (r ^ (r >> 3)) & 7; }
 
 __device__ __forceinline__ float silu_mul_d(float g, float u) {
@@ -90,108 +102,16 @@ __device__ __forceinline__ bf16x8 e4m3x8_bf16(uint2 v) {
     return __builtin_bit_cast(bf16x8, u);
 }
 
-// One unit segment of a launch (routed experts, or shared experts).
-template <int EPI, bool FP8, bool SPLIT>
-__device__ void run_unit(const DecodeSeg& s, const DecodeArgs& d, int group, int blk, int m0,
-                         int rows, int row_base, unsigned char* ring, int lane, int wave,
-                         float* red) {
-    // SPLIT: this wavefront's share of the K groups (split-K over the
-    // workgroup); otherwise the wavefront runs the whole unit alone
-    const int nKall = s.K / kDGroupK;
-    const int kq = SPLIT ? (nKall + kDWaves - 1) / kDWaves : nKall;
-    const int g0 = SPLIT ? min(nKall, wave * kq) : 0, g1 = min(nKall, g0 + kq);
-    const int nK = g1 - g0;
-    const int mrows = min(32, rows - m0);
-    const int r32 = lane & 31, h = lane >> 5;
-    // ---- DMA plan: instruction i covers rows 8i + lane/8, chunk slot lane%8
-    const int dr = lane >> 3, dsl = lane & 7;
-    const char* asrc[4];
-    const char* bsrc[4];
-    const int esz_b = FP8 ? 1 : 2;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 8 * i + dr;                 // row within the 32-row block
-        const int c = dsl ^ dswz(r);              // logical chunk loaded into slot dsl
-        // activation row
-        const int m = min(r, mrows - 1);
-        int64_t arow;
-        if (s.offsets == nullptr) arow = (int64_t)(m0 + m);                        // uniform rows
-        else if (s.gather) arow = (int64_t)(d.row_src[row_base + m0 + m] / d.k_top);  // token of the route
-        else arow = (int64_t)(row_base + m0 + m);
-        asrc[i] = (const char*)s.A + (arow * s.lda) * 2 + c * 16;
-        // weight row
-        int n;
-        if (EPI == EPI_SWIGLU) n = r < 16 ? blk * 16 + r : s.I + blk * 16 + (r - 16);
-        else n = min(blk * 32 + r, s.N_w - 1);
-        // e4m3 rows hold 64 bytes per K group: chunk c < 4 only (slots >= 4 unused)
-        bsrc[i] = (const char*)s.B + ((int64_t)group * s.b_group_stride + (int64_t)n * s.k_seg) * esz_b +
-                  (FP8 ? (c & 3) * 16 : c * 16);
-    }
-    const uint32_t ring0 = __builtin_amdgcn_readfirstlane(lds_addr_d(ring));
-    auto issue = [&](int gk) {
-        const int k0 = (g0 + gk) * kDGroupK;
-        const int seg = k0 / s.k_seg;
-        const int64_t kb = (int64_t)seg * s.b_seg_stride + (k0 - seg * s.k_seg);
-        const uint32_t st = ring0 + (gk % kDStages) * kDStage;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dma16_d(asrc[i] + (int64_t)k0 * 2, __builtin_amdgcn_readfirstlane(st + i * 1024));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dma16_d(bsrc[i] + kb * esz_b, __builtin_amdgcn_readfirstlane(st + 4096 + i * 1024));
-    };
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the ring are done
-#pragma unroll
-    for (int st = 0; st < kDStages - 1; ++st)
-        if (st < nK) issue(st);
-    for (int gk = 0; gk < nK; ++gk) {
-        wait_own(min(kDStages - 2, nK - 1 - gk));
-        const unsigned char* sa = ring + (gk % kDStages) * kDStage;
-        const unsigned char* sb = sa + 4096;
-        bf16x8 af[4], bfr[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = 4 * h + j;
-            af[j] = *(const bf16x8*)(sa + r32 * 128 + ((c ^ dswz(r32)) * 16));
-            if (FP8) {
-                // 8 e4m3 codes at byte (32h + 8j) of the 64-byte row group
-                const int byte = 32 * h + 8 * j;
-                const int cc = byte >> 4;
-                bfr[j] = e4m3x8_bf16(*(const uint2*)(sb + r32 * 128 + ((cc ^ dswz(r32)) * 16) + (byte & 15)));
-            } else {
-                bfr[j] = *(const bf16x8*)(sb + r32 * 128 + ((c ^ dswz(r32)) * 16));
-            }
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage read before it is refilled
-        if (gk + kDStages - 1 < nK) issue(gk + kDStages - 1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[j], acc, 0, 0, 0);
-    }
-
-    // ---- sum the wavefronts' K shares in a fixed order (wave 0 first) ----
-    if (SPLIT) {
-    if (wave > 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[((wave - 1) * 16 + r) * 64 + lane] = acc[r];
-    }
-    __syncthreads();
-    if (wave != 0) {
-        __syncthreads();  // wave 0 has read the partials
-        return;
-    }
-#pragma unroll
-    for (int w = 1; w < kDWaves; ++w)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += red[((w - 1) * 16 + r) * 64 + lane];
-    __syncthreads();
-    }
-
-    // ---- epilogue: lane holds activation row m = lane % 32 ----
-    const int m = r32;
+// Epilogue of one work item: lane holds activation row m = lane % 32 and the
+// weight rows n = 8*(r/4) + 4*(lane/32) + r%4 of acc register r.
+template <int EPI, bool FP8>
+__device__ __forceinline__ void epilogue(const DecodeSeg& s, int group, int blk, int m0, int mrows,
+                                         int row_base, int32_t q, float cw, const f32x16& acc,
+                                         int lane) {
+    const int m = lane & 31;
     if (m >= mrows) return;
     const int64_t orow = (s.offsets == nullptr) ? (int64_t)(m0 + m) : (int64_t)(row_base + m0 + m);
-    const int c4 = 4 * h;
+    const int c4 = 4 * (lane >> 5);
     if (EPI == EPI_SWIGLU) {
         __bf16* o = (__bf16*)s.out + orow * s.ldo + (int64_t)group * s.out_col_per_group;
 #pragma unroll
@@ -212,13 +132,7 @@ __device__ void run_unit(const DecodeSeg& s, const DecodeArgs& d, int group, int
         }
         return;
     }
-    float cw = 1.0f;
-    int64_t drow = orow;
-    if (EPI == EPI_COMBINE) {
-        const int32_t q = d.row_src[orow];
-        cw = d.route_w[q];
-        drow = q;
-    }
+    const int64_t drow = EPI == EPI_COMBINE ? (int64_t)q : orow;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int col = blk * 32 + 8 * q + c4;
@@ -240,41 +154,204 @@ __device__ void run_unit(const DecodeSeg& s, const DecodeArgs& d, int group, int
     }
 }
 
+// One work item: a unit (32 weight rows of one expert) times a block of up to
+// 32 of the expert's activation rows, over this wavefront's K range.
+struct Item {
+    int64_t u;              // unit index over the launch
+    int si, group, blk;     // segment, expert, 32-row weight block
+    int base, rows, m0;     // expert's first row, its row count, this block's first row
+    int mrows;              // rows in this block
+    int g0, nK;             // first K group of this wavefront, K groups
+    int32_t q;              // combine epilogue: route of this lane's row
+    float cw;               // and its weight
+    const char* asrc[4];
+    const char* bsrc[4];
+};
+
 // Units are numbered segment by segment; within a segment, group-major with
 // the 32-row weight blocks fastest.  SPLIT: a workgroup takes one unit at a
 // time and its wavefronts split the unit's K range (each streams a quarter of
 // the weight rows through its own ring; the partial sums meet in LDS), for
-// launches with fewer units than wavefronts.  Otherwise every wavefront takes
-// units on its own (neighbouring wavefronts of a workgroup take neighbouring
-// blocks of one expert and share its activation rows).  Units of experts
-// without rows end at once.
+// launches with few units.  Otherwise every wavefront takes units on its own
+// (neighbouring wavefronts of a workgroup take neighbouring blocks of one
+// expert and share its activation rows).  Work items exist only for experts
+// with rows (the dispatch's 32-row tile table, kept in LDS with the experts'
+// row ranges).
 template <int EPI0, int EPI1, bool FP8, bool SPLIT>
 __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs d) {
     __shared__ __attribute__((aligned(1024))) unsigned char rings[kDWaves][kDStages * kDStage];
     __shared__ float red[SPLIT ? (kDWaves - 1) * 16 * 64 : 1];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t n0 = (int64_t)d.seg[0].n_groups * d.seg[0].blocks;
-    const int64_t n1 = d.n_seg > 1 ? (int64_t)d.seg[1].n_groups * d.seg[1].blocks : 0;
+    // wave index in a scalar register: the work item, and with it the segment
+    // descriptor, is then wave-uniform (scalar loads, no vector-memory wait)
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // tile table and row ranges of segment 0 when it is routed
+    __shared__ int32_t s_mt[kDecodeMaxGroups + 1], s_off[kDecodeMaxGroups + 1];
+    if (d.seg[0].mt) {
+        for (int i = threadIdx.x; i <= d.seg[0].n_groups; i += blockDim.x) {
+            s_mt[i] = d.seg[0].mt[i];
+            s_off[i] = d.seg[0].offsets[i];
+        }
+        __syncthreads();
+    }
+    // work items: 32-row tiles x weight blocks; routed segments own tiles only
+    // for experts with rows (tile table), uniform ones ceil(rows / 32) per group
+    auto items = [&](int si) -> int64_t {
+        const DecodeSeg& s = d.seg[si];
+        const int64_t tiles = s.mt ? (int64_t)(si == 0 ? s_mt[s.n_groups] : s.mt[s.n_groups])
+                                   : (int64_t)s.n_groups * ((s.uniform_rows + kDecodeBM - 1) / kDecodeBM);
+        return tiles * s.blocks;
+    };
+    const int64_t n0 = items(0);
+    const int64_t n1 = d.n_seg > 1 ? items(1) : 0;
+    const int64_t total = n0 + n1;
     const int64_t first = SPLIT ? blockIdx.x : (int64_t)blockIdx.x * kDWaves + wave;
     const int64_t stride = SPLIT ? gridDim.x : (int64_t)gridDim.x * kDWaves;
-    for (int64_t u = first; u < n0 + n1; u += stride) {
-        const int si = u < n0 ? 0 : 1;
-        const DecodeSeg& s = d.seg[si];
-        const int64_t lu = si == 0 ? u : u - n0;
-        const int group = (int)(lu / s.blocks), blk = (int)(lu - (int64_t)group * s.blocks);
-        int rows, base;
-        if (s.offsets) {
-            base = s.offsets[group];
-            rows = s.offsets[group + 1] - base;
+    unsigned char* ring = rings[wave];
+    const uint32_t ring0 = __builtin_amdgcn_readfirstlane(lds_addr_d(ring));
+    const int r32 = lane & 31, h = lane >> 5;
+    const int dr = lane >> 3, dsl = lane & 7;   // DMA: instruction i covers rows 8i + lane/8, chunk slot lane%8
+
+    // this wavefront's K range and DMA sources of the item's block m0
+    auto setup = [&](Item& it, int m0) {
+        const DecodeSeg& s = d.seg[it.si];
+        it.m0 = m0;
+        it.mrows = min(kDecodeBM, it.rows - m0);
+        const int nKall = s.K / kDGroupK;
+        const int kq = SPLIT ? (nKall + kDWaves - 1) / kDWaves : nKall;
+        it.g0 = SPLIT ? min(nKall, wave * kq) : 0;
+        it.nK = min(nKall, it.g0 + kq) - it.g0;
+        const bool fp8 = FP8 && it.si == 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 8 * i + dr;                 // row within the 32-row block
+            const int c = dsl ^ dswz(r);              // logical chunk loaded into slot dsl
+            const int m = min(r, it.mrows - 1);
+            int64_t arow;
+            if (s.offsets == nullptr) arow = (int64_t)(m0 + m);                            // uniform rows
+            else if (s.gather) arow = (int64_t)(d.row_src[it.base + m0 + m] / d.k_top);      // token of the route
+            else arow = (int64_t)(it.base + m0 + m);
+            it.asrc[i] = (const char*)s.A + (arow * s.lda) * 2 + c * 16;
+            int n;
+            if ((it.si == 0 ? EPI0 : EPI1) == EPI_SWIGLU) n = r < 16 ? it.blk * 16 + r : s.I + it.blk * 16 + (r - 16);
+            else n = min(it.blk * 32 + r, s.N_w - 1);
+            // e4m3 rows hold 64 bytes per K group: chunk c < 4 only (slots >= 4 unused)
+            it.bsrc[i] = (const char*)s.B + ((int64_t)it.group * s.b_group_stride + (int64_t)n * s.k_seg) * (fp8 ? 1 : 2) +
+                         (fp8 ? (c & 3) * 16 : c * 16);
+        }
+    };
+    // item u: segment, expert (tile table), 32-row block, weight block
+    auto make = [&](int64_t u, Item& it) {
+        it.u = u;
+        it.si = u < n0 ? 0 : 1;
+        const DecodeSeg& s = d.seg[it.si];
+        const int64_t lu = it.si == 0 ? u : u - n0;
+        const int ti = (int)(lu / s.blocks);
+        it.blk = (int)(lu - (int64_t)ti * s.blocks);
+        int m0;
+        if (s.mt) {
+            // routed segments come first (segment 0): table and row ranges in LDS
+            it.group = __builtin_amdgcn_readfirstlane(find_tile_group(s_mt, s.n_groups, ti));
+            it.base = __builtin_amdgcn_readfirstlane(s_off[it.group]);
+            it.rows = __builtin_amdgcn_readfirstlane(s_off[it.group + 1]) - it.base;
+            m0 = __builtin_amdgcn_readfirstlane((ti - s_mt[it.group]) * kDecodeBM);
         } else {
-            base = 0;
-            rows = s.uniform_rows;
+            const int tpg = (s.uniform_rows + kDecodeBM - 1) / kDecodeBM;
+            it.group = ti / tpg;
+            m0 = (ti - it.group * tpg) * kDecodeBM;
+            it.base = 0;
+            it.rows = s.uniform_rows;
         }
-        if (rows <= 0) continue;  // uniform over the unit's wavefronts
-        for (int m0 = 0; m0 < rows; m0 += 32) {
-            if (si == 0) run_unit<EPI0, FP8, SPLIT>(s, d, group, blk, m0, rows, base, rings[wave], lane, wave, red);
-            else run_unit<EPI1, false, SPLIT>(s, d, group, blk, m0, rows, base, rings[wave], lane, wave, red);
+        setup(it, m0);
+        if ((it.si == 0 ? EPI0 : EPI1) == EPI_COMBINE) {
+            const int m = min(lane & 31, it.mrows - 1);
+            it.q = d.row_src[it.base + m0 + m];
+            it.cw = d.route_w[it.q];
         }
+    };
+    auto issue = [&](const Item& it, int gk, int slot) {
+        const DecodeSeg& s = d.seg[it.si];
+        const bool fp8 = FP8 && it.si == 0;
+        const int k0 = (it.g0 + gk) * kDGroupK;
+        const int seg = k0 / s.k_seg;
+        const int64_t kb = (int64_t)seg * s.b_seg_stride + (k0 - seg * s.k_seg);
+        const uint32_t st = ring0 + slot * kDStage;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16_d(it.asrc[i] + (int64_t)k0 * 2, __builtin_amdgcn_readfirstlane(st + i * 1024));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dma16_d(it.bsrc[i] + kb * (fp8 ? 1 : 2), __builtin_amdgcn_readfirstlane(st + 4096 + i * 1024));
+    };
+
+    Item cur, nxt;
+    if (first >= total) return;   // SPLIT: the same for every wavefront of the workgroup
+    make(first, cur);
+    int issued = 0, consumed = 0;  // stages of this wavefront's stream
+    int pre = 0;                   // stages of `cur` already issued
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    while (true) {
+        for (; pre < min(kDStages - 1, cur.nK); ++pre) issue(cur, pre, (issued++) & (kDStages - 1));
+        const bool has_next = cur.u + stride < total;
+        const bool cur_fp8 = FP8 && cur.si == 0;
+
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+        for (int gk = 0; gk < cur.nK; ++gk) {
+            wait_own(min(kDStages - 2, cur.nK - 1 - gk));
+            const unsigned char* sa = ring + (consumed & (kDStages - 1)) * kDStage;
+            const unsigned char* sb = sa + 4096;
+            bf16x8 af[4], bfr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = 4 * h + j;
+                af[j] = *(const bf16x8*)(sa + r32 * 128 + ((c ^ dswz(r32)) * 16));
+                if (cur_fp8) {
+                    // 8 e4m3 codes at byte (32h + 8j) of the 64-byte row group
+                    const int byte = 32 * h + 8 * j;
+                    const int cc = byte >> 4;
+                    bfr[j] = e4m3x8_bf16(*(const uint2*)(sb + r32 * 128 + ((cc ^ dswz(r32)) * 16) + (byte & 15)));
+                } else {
+                    bfr[j] = *(const bf16x8*)(sb + r32 * 128 + ((c ^ dswz(r32)) * 16));
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage read before it is refilled
+            ++consumed;
+            const int s3 = gk + kDStages - 1;
+            if (s3 < cur.nK) issue(cur, s3, (issued++) & (kDStages - 1));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[j], acc, 0, 0, 0);
+        }
+
+        // ---- sum the wavefronts' K shares in a fixed order (wave 0 first) ----
+        bool owner = true;
+        if (SPLIT) {
+            if (wave > 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) red[((wave - 1) * 16 + r) * 64 + lane] = acc[r];
+            }
+            __syncthreads();
+            if (wave == 0) {
+#pragma unroll
+                for (int w = 1; w < kDWaves; ++w)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[r] += red[((w - 1) * 16 + r) * 64 + lane];
+            }
+            __syncthreads();
+            owner = wave == 0;
+        }
+        if (owner) {
+            if (cur.si == 0)
+                epilogue<EPI0, FP8>(d.seg[0], cur.group, cur.blk, cur.m0, cur.mrows, cur.base, cur.q, cur.cw, acc, lane);
+            else
+                epilogue<EPI1, false>(d.seg[1], cur.group, cur.blk, cur.m0, cur.mrows, cur.base, cur.q, cur.cw, acc, lane);
+        }
+        if (!has_next) break;
+        // the next item is set up with nothing of this wavefront's ring in
+        // flight: its lookups (row gather, combine weights) are plain loads
+        // whose waits would otherwise drain the ring
+        make(cur.u + stride, nxt);
+        cur = nxt;
+        pre = 0;
     }
 }
 
