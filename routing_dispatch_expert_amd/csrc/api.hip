@@ -66,6 +66,11 @@ moe_status check_problem(const moe_problem* pp) {
     if (p.n_shared > 0 && p.I_shared % 128) return MOE_ERR_UNSUPPORTED;
     const int64_t Q = (int64_t)p.T * p.k;
     if (Q >= INT_MAX / 2) return MOE_ERR_UNSUPPORTED;  // route and row indices are int32
+    // one expert's weight matrix is addressed with 32-bit offsets in the GEMMs
+    const int64_t wb = p.w_dtype == MOE_F32 ? 4 : 2;
+    const int64_t lim = (int64_t)1 << 31;
+    if (2 * (int64_t)p.I * p.H * wb >= lim) return MOE_ERR_UNSUPPORTED;
+    if (p.n_shared > 0 && 2 * (int64_t)p.I_shared * p.H * 4 >= lim) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 

@@ -44,7 +44,6 @@ namespace rde {
 namespace {
 
 constexpr int BM = kGemmBM, BN = 256, BK = 32;
-constexpr int kThreads = 512;   // 8 waves: 2 (M) x 4 (N)
 constexpr int kMaxGroupsLds = 1024;
 
 // Largest g with s_mt[g] * nt <= L (s_mt non-decreasing, s_mt[0] = 0).
@@ -135,10 +134,9 @@ template <int N>
 __device__ __forceinline__ void waitcnt_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-// The same with a count known only at run time (0 .. 10).
+// The same with a count known only at run time (0 .. 16).
 __device__ __forceinline__ void wait_barrier_dyn(int n) {
     switch (n) {
-        case 0: waitcnt_barrier<0>(); break;
         case 1: waitcnt_barrier<1>(); break;
         case 2: waitcnt_barrier<2>(); break;
         case 3: waitcnt_barrier<3>(); break;
@@ -149,6 +147,12 @@ __device__ __forceinline__ void wait_barrier_dyn(int n) {
         case 8: waitcnt_barrier<8>(); break;
         case 9: waitcnt_barrier<9>(); break;
         case 10: waitcnt_barrier<10>(); break;
+        case 11: waitcnt_barrier<11>(); break;
+        case 12: waitcnt_barrier<12>(); break;
+        case 13: waitcnt_barrier<13>(); break;
+        case 14: waitcnt_barrier<14>(); break;
+        case 15: waitcnt_barrier<15>(); break;
+        case 16: waitcnt_barrier<16>(); break;
         default: waitcnt_barrier<0>(); break;   // never smaller than needed
     }
 }
@@ -165,14 +169,24 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint2 v) {
 // rows wn*64 .. wn*64+63.  The MFMA is issued as B x A^T so each lane ends
 // with 4 consecutive output columns of one row: for acc register r of a
 // 32x32 block, row = lane % 32, column = 8*(r/4) + 4*(lane/32) + r%4.
-template <int EPI, bool FP8>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
+//
+// NW is the number of waves (2 x NW/2).  NW = 4 gives 128 x 128 wave tiles
+// (a third fewer LDS fragment reads per MFMA); with one wave per SIMD and no
+// explicit fragment double-buffering it measured slower than NW = 8 at every
+// batch size, so only NW = 8 is built.  With NW = 4 every A row group of a
+// tile would be loaded.
+template <int EPI, bool FP8, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
+    constexpr int NT = NW * 64;                  // threads
     constexpr int B_STAGE = FP8 ? B_STAGE_E4M3 : B_STAGE_BF16;
-    constexpr int LB = FP8 ? 1 : 2;  // B DMA instructions per thread per k-tile
+    constexpr int BW = BN / (NW / 2);            // B rows (wave tile columns) per wave: 64 or 128
+    constexpr int NBW = BW / 32;                 // 32-column MFMA blocks per wave: 2 or 4
+    constexpr int LB = (FP8 ? 8 : 16) / NW;      // B DMA instructions per thread per k-tile
+    constexpr int GA = 16 / NW;                  // A 16-row groups per wave: 2 or 4
     __shared__ __attribute__((aligned(1024))) unsigned char sA[kStages][A_STAGE];
     __shared__ __attribute__((aligned(1024))) unsigned char sB[kStages][B_STAGE];
-    __shared__ int32_t s_mt[kMaxGroupsLds + 1];
-    __shared__ __attribute__((aligned(16))) unsigned char sOut[kThreads / 64][32 * kOutPitch];
+    __shared__ int32_t s_mt[kMaxGroupsLds + 1], s_off[kMaxGroupsLds + 1];
+    __shared__ __attribute__((aligned(16))) unsigned char sOut[NW][32 * kOutPitch];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -182,7 +196,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         tiles_per_group = (a.uniform_rows + BM - 1) / BM;
         total_mt = tiles_per_group * a.n_groups;
     } else {
-        for (int i = tid; i <= a.n_groups; i += kThreads) s_mt[i] = a.mt_off[i];
+        for (int i = tid; i <= a.n_groups; i += NT) {
+            s_mt[i] = a.mt_off[i];
+            s_off[i] = a.offsets[i];   // row ranges: LDS reads in the tile set-up
+        }
         __syncthreads();
         total_mt = s_mt[a.n_groups];
     }
@@ -200,23 +217,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     const char* Bb = (const char*)a.B;
     const int nk = a.K / BK;
 
-    // DMA plan.  A: wave w fills the 16-row groups w and w + 8 (row
-    // 16*group + lane/4); a group wholly past the expert's last row is not
-    // loaded, so a half-filled tile issues half the A traffic and every wave
-    // still has one A group while rows > 128.  bf16 B: wave w fills rows
-    // w*32 + 16*b + lane/4 (b = 0, 1).  e4m3 B: wave w fills rows w*32 +
-    // lane/2, 16-byte half lane%2 (one instruction per k-tile).
+    // DMA plan.  A: wave w fills the 16-row groups w + NW*i (row 16*group +
+    // lane/4), i < GA; with 8 waves a group wholly past the expert's last row
+    // is not loaded, so a half-filled tile issues half the A traffic and
+    // every wave still has one A group while rows > 128.  bf16 B: wave w
+    // fills rows w*16*LB + 16*b + lane/4 (b < LB).  e4m3 B: wave w fills rows
+    // w*32*LB + 32*b + lane/2, 16-byte half lane%2.
     const int dr = lane >> 2, ds = lane & 3;
 
     // wave-uniform LDS bases of this wave's DMA blocks in ring slot 0
     const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(sA[0]) + wave * 1024);
-    const uint32_t lb0 = __builtin_amdgcn_readfirstlane(lds_addr(sB[0]) + wave * (FP8 ? 1024 : 2048));
+    const uint32_t lb0 = __builtin_amdgcn_readfirstlane(lds_addr(sB[0]) + wave * LB * 1024);
 
     // A tile's place in the problem and this thread's DMA sources (byte
-    // offsets at k = 0).  la = A groups this wave loads (0, 1 or 2).
+    // offsets at k = 0).  la = A groups this wave loads (0 .. GA).
     struct Tile {
         int g, nt, a_row0, rows, rot, la;
-        int64_t ga0, ga1, gb0, gb1;
+        int64_t ga[GA];
+        int64_t gbase;          // the expert's weights (wave-uniform)
+        uint32_t gb[LB];        // per-lane weight offsets within them
     };
     auto make_tile = [&](int64_t Lt) {
         Tile t;
@@ -230,40 +249,53 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
             t.a_row0 = ml * BM;
             t.rows = min(BM, a.uniform_rows - t.a_row0);
         } else {
-            t.g = find_group(s_mt, a.n_groups, Lt, ntl);
+            t.g = __builtin_amdgcn_readfirstlane(find_group(s_mt, a.n_groups, Lt, ntl));
             cnt = s_mt[t.g + 1] - s_mt[t.g];
             const int loc = (int)(Lt - (int64_t)s_mt[t.g] * ntl);
             t.nt = loc / cnt;
             ml = loc - t.nt * cnt;
-            const int e0 = a.offsets[t.g], e1 = a.offsets[t.g + 1];
+            const int e0 = s_off[t.g], e1 = s_off[t.g + 1];
             t.a_row0 = e0 + ml * BM;
             t.rows = min(BM, e1 - t.a_row0);
         }
         const int g = t.g, nt = t.nt, rows = t.rows;
+        // B row r of the tile: for SwiGLU each wave's BW rows are BW/2 gate
+        // rows and the matching BW/2 up rows
         auto brow_of = [&](int r) {
             if (EPI == EPI_SWIGLU) {
-                const int w2 = r >> 6, rr = r & 63;
-                return (rr < 32) ? (nt * 128 + w2 * 32 + rr) : (a.I + nt * 128 + w2 * 32 + rr - 32);
+                const int w2 = r / BW, rr = r % BW;
+                return (rr < BW / 2) ? (nt * 128 + w2 * (BW / 2) + rr)
+                                     : (a.I + nt * 128 + w2 * (BW / 2) + rr - BW / 2);
             }
             return min(nt * BN + r, a.N_w - 1);   // rows past N (ragged last tile): clamped
         };
-        const int ra0 = wave * 16 + dr, ra1 = ra0 + 128;
-        int64_t ar0 = t.a_row0 + min(ra0, rows - 1), ar1 = t.a_row0 + min(ra1, rows - 1);
-        if (a.gather) {  // expert rows read in place: the token of each route
-            ar0 = a.row_src[ar0] / a.k_top;
-            ar1 = a.row_src[ar1] / a.k_top;
+        // A rows: with gather, the tokens of the tile's routes, all looked up
+        // before any is used (one wait for the lookups)
+        int64_t ar[GA];
+#pragma unroll
+        for (int i = 0; i < GA; ++i) ar[i] = t.a_row0 + min((wave + NW * i) * 16 + dr, rows - 1);
+        if (a.gather) {
+            int32_t q[GA];
+#pragma unroll
+            for (int i = 0; i < GA; ++i) q[i] = a.row_src[ar[i]];
+#pragma unroll
+            for (int i = 0; i < GA; ++i) ar[i] = q[i] / a.k_top;
         }
-        t.ga0 = ar0 * a.lda * 2 + ((ds ^ swz(ra0)) * 16);
-        t.ga1 = ar1 * a.lda * 2 + ((ds ^ swz(ra1)) * 16);
-        const int64_t gbase = (int64_t)g * a.b_group_stride;
-        t.gb1 = 0;
-        if (FP8) {
-            const int rb = wave * 32 + (lane >> 1), hb = lane & 1;
-            t.gb0 = (gbase + (int64_t)brow_of(rb) * a.k_seg) + ((hb ^ ((rb >> 2) & 1)) * 16);
-        } else {
-            const int rb0 = wave * 32 + dr, rb1 = rb0 + 16;
-            t.gb0 = (gbase + (int64_t)brow_of(rb0) * a.k_seg) * 2 + ((ds ^ swz(rb0)) * 16);
-            t.gb1 = (gbase + (int64_t)brow_of(rb1) * a.k_seg) * 2 + ((ds ^ swz(rb1)) * 16);
+#pragma unroll
+        for (int i = 0; i < GA; ++i) {
+            const int ra = (wave + NW * i) * 16 + dr;
+            t.ga[i] = ar[i] * a.lda * 2 + ((ds ^ swz(ra)) * 16);
+        }
+        t.gbase = (int64_t)g * a.b_group_stride * (FP8 ? 1 : 2);
+#pragma unroll
+        for (int b = 0; b < LB; ++b) {
+            if (FP8) {
+                const int rb = wave * 32 * LB + 32 * b + (lane >> 1), hb = lane & 1;
+                t.gb[b] = (uint32_t)brow_of(rb) * (uint32_t)a.k_seg + ((hb ^ ((rb >> 2) & 1)) * 16);
+            } else {
+                const int rb = wave * 16 * LB + 16 * b + dr;
+                t.gb[b] = (uint32_t)brow_of(rb) * (uint32_t)a.k_seg * 2 + ((ds ^ swz(rb)) * 16);
+            }
         }
         // K order: the tile starts at k-tile `rot` and wraps.  Tiles of
         // different experts running at the same time then read different
@@ -274,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         // fetched into L2 once and reused.  rot depends only on the expert, so
         // a row's summation order never depends on the other tokens.
         t.rot = (g * 13) % nk;
-        t.la = __builtin_amdgcn_readfirstlane((16 * wave < rows) + (16 * (wave + 8) < rows));
+        t.la = NW == 8 ? __builtin_amdgcn_readfirstlane((16 * wave < rows) + (16 * (wave + 8) < rows)) : GA;
         return t;
     };
     // Load k-tile s (in the tile's own K order) of tile t into ring slot `slot`.
@@ -285,14 +317,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         const int seg = k0 / a.k_seg;
         const int64_t bo = (int64_t)seg * a.b_seg_stride + (k0 - seg * a.k_seg);
         const uint32_t la = la0 + slot * A_STAGE, lb = lb0 + slot * B_STAGE;
-        if (t.la >= 1) dma16(Ab + t.ga0 + (int64_t)k0 * 2, la);
-        if (t.la >= 2) dma16(Ab + t.ga1 + (int64_t)k0 * 2, la + 8192);
-        if (FP8) {
-            dma16(Bb + t.gb0 + bo, lb);
-        } else {
-            dma16(Bb + t.gb0 + bo * 2, lb);
-            dma16(Bb + t.gb1 + bo * 2, lb + 1024);
-        }
+#pragma unroll
+        for (int i = 0; i < GA; ++i)
+            if (t.la > i) dma16(Ab + t.ga[i] + (int64_t)k0 * 2, la + i * NW * 1024);
+#pragma unroll
+        for (int b = 0; b < LB; ++b) dma16(Bb + t.gbase + t.gb[b] + bo * (FP8 ? 1 : 2), lb + b * 1024);
     };
 
     // The load ring runs across tiles: while a tile's last kStages - 1
@@ -316,17 +345,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         const int cn = has_next ? LB + nxt.la : 0;   // next tile's DMA count per k-tile
         const int g = cur.g, nt = cur.nt, a_row0 = cur.a_row0, rows = cur.rows;
 
-        f32x16 acc[4][2];
+        f32x16 acc[4][NBW];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NBW; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
         // active row blocks of this wave: wm + 2*mb is active iff 32*(wm + 2*mb) < rows,
         // i.e. mb < n_act (a prefix); waves whose 64 B rows lie past N (ragged last
         // n-tile) have none.  Wave-uniform, kept in a scalar register.
-        const bool col_ok = EPI == EPI_SWIGLU || nt * BN + wn * 64 < a.N_w;
+        const bool col_ok = EPI == EPI_SWIGLU || nt * BN + wn * BW < a.N_w;
         const int n_act = __builtin_amdgcn_readfirstlane(
             col_ok ? max(0, min(4, (rows - 32 * wm + 63) / 64)) : 0);
 
@@ -352,17 +381,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < BK / 16; ++ks) {
                     const int c = ks * 2 + half;  // logical 16-byte chunk of this lane
-                    bf16x8 b0, b1, av[NA > 0 ? NA : 1];
-                    const int r0 = wn * 64 + rA, r1 = r0 + 32;
-                    if (FP8) {
-                        // piece c (8 bytes) of a 32-byte row; halves swapped on row bit 2
-                        const int p0 = ((c >> 1) ^ ((r0 >> 2) & 1)) * 16 + (c & 1) * 8;
-                        const int p1 = ((c >> 1) ^ ((r1 >> 2) & 1)) * 16 + (c & 1) * 8;
-                        b0 = e4m3x8_to_bf16x8(*(const uint2*)(sb + r0 * 32 + p0));
-                        b1 = e4m3x8_to_bf16x8(*(const uint2*)(sb + r1 * 32 + p1));
-                    } else {
-                        b0 = *(const bf16x8*)(sb + r0 * 64 + ((c ^ swz(r0)) * 16));
-                        b1 = *(const bf16x8*)(sb + r1 * 64 + ((c ^ swz(r1)) * 16));
+                    bf16x8 bv[NBW], av[NA > 0 ? NA : 1];
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb) {
+                        const int r = wn * BW + nb * 32 + rA;
+                        if (FP8) {
+                            // piece c (8 bytes) of a 32-byte row; halves swapped on row bit 2
+                            const int pc = ((c >> 1) ^ ((r >> 2) & 1)) * 16 + (c & 1) * 8;
+                            bv[nb] = e4m3x8_to_bf16x8(*(const uint2*)(sb + r * 32 + pc));
+                        } else {
+                            bv[nb] = *(const bf16x8*)(sb + r * 64 + ((c ^ swz(r)) * 16));
+                        }
                     }
 #pragma unroll
                     for (int mb = 0; mb < NA; ++mb) {
@@ -370,15 +399,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
                         av[mb] = *(const bf16x8*)(sa + ra * 64 + ((c ^ swz(ra)) * 16));
                     }
 #pragma unroll
-                    for (int mb = 0; mb < NA; ++mb) {
-                        acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, av[mb], acc[mb][0], 0, 0, 0);
-                        acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, av[mb], acc[mb][1], 0, 0, 0);
-                    }
+                    for (int mb = 0; mb < NA; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < NBW; ++nb)
+                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[nb], av[mb], acc[mb][nb], 0, 0, 0);
                 }
             }
         };
         auto by_la = [&](auto na_c) {
-            if (cur.la == 2) kloop(na_c, std::integral_constant<int, 2>{});
+            if (NW != 8) kloop(na_c, std::integral_constant<int, GA>{});   // every A group loaded
+            else if (cur.la == 2) kloop(na_c, std::integral_constant<int, 2>{});
             else if (cur.la == 1) kloop(na_c, std::integral_constant<int, 1>{});
             else kloop(na_c, std::integral_constant<int, 0>{});
         };
@@ -408,10 +438,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
             if (EPI == EPI_F32) {
                 if (row >= rows) continue;
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int col = nt * BN + wn * 64 + nb * 32 + 8 * i + c4;
+                        const int col = nt * BN + wn * BW + nb * 32 + 8 * i + c4;
                         float v[4];
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
@@ -428,11 +458,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
                 q = a.row_src[orow];
                 cw = a.route_w[q];
             }
-            constexpr int NB = EPI == EPI_SWIGLU ? 1 : 2;
+            // SwiGLU: gate block nb pairs with up block nb + NBW/2
+            constexpr int NB = EPI == EPI_SWIGLU ? NBW / 2 : NBW;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
+                // one 32 x 32 block at a time: the scheduler may not hoist the
+                // accumulator reads of later blocks (they would all be live)
+                __builtin_amdgcn_sched_barrier(0);
                 // output columns of this 32-column block
-                const int col0 = EPI == EPI_SWIGLU ? nt * 128 + wn * 32 : nt * BN + wn * 64 + nb * 32;
+                const int col0 = EPI == EPI_SWIGLU ? nt * 128 + wn * (BW / 2) + nb * 32 : nt * BN + wn * BW + nb * 32;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int col = col0 + 8 * i + c4;
@@ -440,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         if (EPI == EPI_SWIGLU) {
-                            float gv = acc[mb][0][4 * i + j], uv = acc[mb][1][4 * i + j];
+                            float gv = acc[mb][nb][4 * i + j], uv = acc[mb][nb + NBW / 2][4 * i + j];
                             if (FP8) {
                                 gv *= a.bscale[(int64_t)g * a.N_w + col + j];
                                 uv *= a.bscale[(int64_t)g * a.N_w + a.I + col + j];
@@ -584,10 +618,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int w_dtype, int grid, hipStream_t s) {
     const bool fp8 = w_dtype == MOE_E4M3;
-#define RDE_GEMM_CASE(E)                                                                      \
-    case E:                                                                                   \
-        if (fp8) hipLaunchKernelGGL((gemm_bf16_kernel<E, true>), dim3(grid), dim3(kThreads), 0, s, a); \
-        else hipLaunchKernelGGL((gemm_bf16_kernel<E, false>), dim3(grid), dim3(kThreads), 0, s, a);   \
+#define RDE_GEMM_CASE(E)                                                                                  \
+    case E:                                                                                               \
+        if (fp8) hipLaunchKernelGGL((gemm_bf16_kernel<E, true, 8>), dim3(grid), dim3(512), 0, s, a);      \
+        else hipLaunchKernelGGL((gemm_bf16_kernel<E, false, 8>), dim3(grid), dim3(512), 0, s, a);         \
         break;
     switch (a.epi) {
         RDE_GEMM_CASE(EPI_SWIGLU)
