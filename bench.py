@@ -68,7 +68,7 @@ def stage_bytes_flops(cs, R, touched, ab, wb):
     return st
 
 
-def run_workload(name, steps, warmup, with_events=True):
+def run_workload(name, steps, warmup, with_events=True, protocols=False):
     import torch
     import routing_dispatch_expert_amd as rde
     import synth
@@ -124,6 +124,7 @@ def run_workload(name, steps, warmup, with_events=True):
             step(i, evs[i])
         torch.cuda.synchronize()
         wall_ev = time.perf_counter() - t0
+    proto = measure_protocols(step, torch) if protocols else None
     if rde.moe_error(ws) != 0:
         raise RuntimeError("malformed routes reported on synthetic inputs")
     stages = {}
@@ -138,7 +139,50 @@ def run_workload(name, steps, warmup, with_events=True):
     ab = 4 if cs.act_fmt == synth.FMT_F32 else 2
     wb = {synth.FMT_F32: 4, synth.FMT_BF16: 2, synth.FMT_E4M3: 1}[cs.w_fmt]
     return dict(cs=cs, steps=steps, wall=wall, wall_ev=wall_ev, stages=stages, R=R, touched=touched,
-                bf=stage_bytes_flops(cs, R, touched, ab, wb), base=base)
+                bf=stage_bytes_flops(cs, R, touched, ab, wb), base=base, protocols=proto)
+
+
+def measure_protocols(step, torch, groups=15, calls=20, graph_calls=64, graph_replays=10):
+    """Two further views of the same call.
+    cold: a 1 GiB device write before every call evicts L2 and the 256 MB
+          last-level cache, and the call alone is timed with events on the
+          stream it runs on (groups x calls samples; median and p95).
+    graph: graph_calls back-to-back calls, rotating over the input banks,
+          captured once into a HIP graph and replayed (launch cost amortised)."""
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
+    cold = []
+    for g in range(groups):
+        for c in range(calls):
+            flush.fill_((g * calls + c) & 0xFF)
+            e0[c].record()
+            step(c)
+            e1[c].record()
+        torch.cuda.synchronize()
+        cold += [e0[c].elapsed_time(e1[c]) * 1e3 for c in range(calls)]
+    del flush
+    cold.sort()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(graph_calls):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(graph_replays):
+        g.replay()
+    torch.cuda.synchronize()
+    per_call = (time.perf_counter() - t0) / (graph_replays * graph_calls)
+    return {"cold_us_median": round(cold[len(cold) // 2], 2),
+            "cold_us_p95": round(cold[int(len(cold) * 0.95)], 2),
+            "cold_samples": f"{groups} x {calls} calls, a 1 GiB device write before each",
+            "graph_us_per_call": round(per_call * 1e6, 2),
+            "graph_calls": f"{graph_calls} calls captured in one graph, {graph_replays} replays"}
 
 
 def kernel_source_sha256() -> str:
@@ -254,7 +298,7 @@ def main():
         del src, dst
     print(f"[bench] workload {args.workload}: warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
-    res = run_workload(args.workload, args.steps, args.warmup)
+    res = run_workload(args.workload, args.steps, args.warmup, protocols=True)
     cs = res["cs"]
     ms = res["wall"] / args.steps * 1e3
     summ = summary(res)
@@ -275,6 +319,10 @@ def main():
         **summ,
         "roofline": roofline_of(res, dom),
     }
+    if res.get("protocols"):
+        pr = dict(res["protocols"])
+        pr["graph_tokens_per_s"] = round(cs.T / (pr["graph_us_per_call"] * 1e-6), 1)
+        line["protocols"] = pr
     print(f"[bench] {cs.name}: {ms*1e3:.1f} us/step, stages {summ['stages_us']}",
           file=sys.stderr, flush=True)
     if args.cpu_tokens > 0:
