@@ -133,9 +133,7 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
     }
     // malformed routes: one atomic per wave
     const uint64_t badm = __ballot(n_bad > 0);
-    int wave_bad = n_bad;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) wave_bad += __shfl_xor(wave_bad, off, kWave);
+    const int wave_bad = wave_sum_i32(n_bad);
     if (badm && lane == 0) atomicAdd(&ctrl[CTRL_BAD_ROUTES], wave_bad);
     __syncthreads();
     for (int e = tid; e < E; e += blockDim.x) {
@@ -403,9 +401,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_dispatch_kernel(
         rank_w[it] = r;
         ex[it] = e;
     }
-    int wave_bad = n_bad;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) wave_bad += __shfl_xor(wave_bad, off, kWave);
+    const int wave_bad = wave_sum_i32(n_bad);
     if (wave_bad && lane == 0) atomicAdd(&ctrl[CTRL_BAD_ROUTES], wave_bad);
     __syncthreads();
 
