@@ -378,9 +378,10 @@ hipError_t run_decode(const DecodeSeg* a, const DecodeSeg* b, const int32_t* row
     if (d.n_seg > 1 && d.seg[1].offsets) return hipErrorInvalidValue;
     if (d.seg[0].offsets && (!d.seg[0].mt || d.seg[0].n_groups > kDecodeMaxGroups)) return hipErrorInvalidValue;
     // Split K over a workgroup's 4 wavefronts when the launch has fewer units
-    // than the chip has wavefronts and each wavefront still gets >= 8 K groups
-    // of 64 (a longer stream per wavefront keeps its ring full).  The number of
-    // touched experts is on the device; the host bounds it by min(E, T*k).
+    // than the chip has wavefronts and each wavefront still gets >= 5 K groups
+    // of 64 (K >= 1280; shorter streams are mostly ring fill, and measured
+    // slower split than whole).  The number of touched experts is on the
+    // device; the host bounds it by min(E, T*k).
     int64_t units = 0;
     int kmin = INT_MAX;
     for (int i = 0; i < d.n_seg; ++i) {
@@ -389,7 +390,7 @@ hipError_t run_decode(const DecodeSeg* a, const DecodeSeg* b, const int32_t* row
         units += groups * g.blocks;
         kmin = std::min(kmin, g.K);
     }
-    const int split = (units < (int64_t)decode_grid() * 4 && kmin >= 2048) ? 1 : 0;
+    const int split = (units < (int64_t)decode_grid() * 4 && kmin >= 1280) ? 1 : 0;
     // the shared experts are always bf16; a segment list that starts with them
     // runs the bf16 instantiation
     return launch_decode_gemm(d, a ? w_dtype : MOE_BF16, split, decode_grid(), s);

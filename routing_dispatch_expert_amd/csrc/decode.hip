@@ -172,9 +172,10 @@ struct Item {
 // the 32-row weight blocks fastest.  SPLIT: a workgroup takes one unit at a
 // time and its wavefronts split the unit's K range (each streams a quarter of
 // the weight rows through its own ring; the partial sums meet in LDS), for
-// launches with few units.  Otherwise every wavefront takes units on its own
-// (neighbouring wavefronts of a workgroup take neighbouring blocks of one
-// expert and share its activation rows).  Work items exist only for experts
+// launches with few units.  Otherwise every wavefront takes units on its own,
+// dealt to workgroups first (unit u to workgroup u % grid, wavefront
+// u / grid), so that a launch with fewer units than wavefronts still spreads
+// them over every CU.  Work items exist only for experts
 // with rows (the dispatch's 32-row tile table, kept in LDS with the experts'
 // row ranges).
 template <int EPI0, int EPI1, bool FP8, bool SPLIT>
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     const int64_t n0 = items(0);
     const int64_t n1 = d.n_seg > 1 ? items(1) : 0;
     const int64_t total = n0 + n1;
-    const int64_t first = SPLIT ? blockIdx.x : (int64_t)blockIdx.x * kDWaves + wave;
+    const int64_t first = SPLIT ? blockIdx.x : (int64_t)wave * gridDim.x + blockIdx.x;
     const int64_t stride = SPLIT ? gridDim.x : (int64_t)gridDim.x * kDWaves;
     unsigned char* ring = rings[wave];
     const uint32_t ring0 = __builtin_amdgcn_readfirstlane(lds_addr_d(ring));
