@@ -39,6 +39,8 @@ def parse():
                     help="comma-separated extra workloads timed briefly ('' = none)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
+    ap.add_argument("--protocols", type=int, default=1,
+                    help="1: also time cold calls (median/p95) and a captured graph of calls")
     ap.add_argument("--cpu-tokens", type=int, default=128,
                     help="tokens of the CPU oracle sample (0 = skip)")
     return ap.parse_args()
@@ -298,7 +300,7 @@ def main():
         del src, dst
     print(f"[bench] workload {args.workload}: warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
-    res = run_workload(args.workload, args.steps, args.warmup, protocols=True)
+    res = run_workload(args.workload, args.steps, args.warmup, protocols=bool(args.protocols))
     cs = res["cs"]
     ms = res["wall"] / args.steps * 1e3
     summ = summary(res)
