@@ -5,10 +5,13 @@ expert GEMMs; the others run the tiled grouped GEMM; both are covered.
 
 Each test prints the case it runs before touching the GPU.  Small cases are
 compared element by element against the full oracle; they span several
-128-row m-tiles with a ragged last tile, several k-tiles and n-tiles.  The
+m-tiles (256 rows for bf16, 64 for float32) with a ragged last tile, several
+k-tiles and n-tiles.  The
 full-size workloads (the pages' shapes) are compared bit-exactly on all
 routing / dispatch metadata and on sampled token rows for the FFN outputs.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -101,7 +104,7 @@ def test_route_pm16_bit_exact():
         assert torch.all(w.cpu() == torch.tensor(1.0, dtype=torch.float32) / 9)
 
 
-@pytest.mark.parametrize("E,k", [(7, 3), (64, 6), (200, 9), (1024, 32)])
+@pytest.mark.parametrize("E,k", [(7, 3), (9, 9), (32, 32), (64, 6), (130, 32), (200, 9), (1024, 32)])
 def test_route_ties_and_special_values(E, k):
     _say("route ties", E, k)
     g = torch.Generator().manual_seed(E)
@@ -117,7 +120,7 @@ def test_route_ties_and_special_values(E, k):
     assert_f32_close(w, ow, "w")
 
 
-@pytest.mark.parametrize("E,k", [(7, 3), (64, 6), (240, 9), (1024, 32)])
+@pytest.mark.parametrize("E,k", [(7, 3), (9, 9), (32, 32), (64, 6), (130, 32), (240, 9), (1024, 32)])
 def test_route_sigmoid_ties_and_special_values(E, k):
     # large logits saturate the float32 score to 1.0 (ties decided by index),
     # grid biases make score + bias exact ties too; NaN and +-inf included
@@ -136,6 +139,22 @@ def test_route_sigmoid_ties_and_special_values(E, k):
         oi, ow = _oracle_route(cs, lg.numpy(), b)
         np.testing.assert_array_equal(np_i32(ids), oi)
         assert_f32_close(w, ow, "w")
+
+
+@pytest.mark.parametrize("T,E,k", [(5, 9, 9), (40, 240, 9), (64, 64, 6), (33, 512, 32)])
+def test_forward_small_batch_routing_ties(T, E, k):
+    # the single-workgroup dispatch of small batches routes several tokens per
+    # wavefront; its routes are compared through the forward's metadata
+    _say("small-batch routing ties", T, E, k)
+    g = torch.Generator().manual_seed(7 * E + T)
+    pool = torch.tensor([-1.0, -0.0, 0.0, 1.0, 2.5, float("-inf"), float("nan")])
+    lg = pool[torch.randint(0, len(pool), (T, E), generator=g)]
+    cs = synth.Case("small_ties", T=T, H=128, E=E, k=k, I=128, C=T)
+    inp = dataclasses.replace(synth.make_inputs(cs, DEV), logits=lg.to(DEV))
+    _, meta, _ = _forward_gpu(cs, inp)
+    oi, ow = oracle.route(lg.numpy(), k)
+    np.testing.assert_array_equal(np_i32(meta["ids"]), oi)
+    assert_f32_close(meta["w"], ow, "w")
 
 
 # ---- dispatch ----------------------------------------------------------------
