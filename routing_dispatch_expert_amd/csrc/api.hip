@@ -362,8 +362,11 @@ DecodeSeg shared_seg2(const moe_problem& p, const void* h_sh, const void* w2_sh,
     return s;
 }
 
+// max_rows: a bound on the rows of any group known to hold (-1: none); 8 or
+// fewer selects the 8-row activation staging.
 hipError_t run_decode(const DecodeSeg* a, const DecodeSeg* b, const int32_t* row_src, int k,
-                      const float* route_w, int w_dtype, int64_t route_count, hipStream_t s) {
+                      const float* route_w, int w_dtype, int64_t route_count, int max_rows,
+                      hipStream_t s) {
     DecodeArgs d = {};
     d.seg[0] = a ? *a : *b;
     d.n_seg = 1;
@@ -393,7 +396,8 @@ hipError_t run_decode(const DecodeSeg* a, const DecodeSeg* b, const int32_t* row
     const int split = (units < (int64_t)decode_grid() * 4 && kmin >= 1280) ? 1 : 0;
     // the shared experts are always bf16; a segment list that starts with them
     // runs the bf16 instantiation
-    return launch_decode_gemm(d, a ? w_dtype : MOE_BF16, split, decode_grid(), s);
+    const int small_m = (max_rows >= 0 && max_rows <= 8) ? 1 : 0;
+    return launch_decode_gemm(d, a ? w_dtype : MOE_BF16, split, small_m, decode_grid(), s);
 }
 
 moe_status check_ptrs16(std::initializer_list<const void*> ps) {
@@ -482,9 +486,9 @@ moe_status moe_expert_ffn(const moe_problem* p, const void* x_disp, const int32_
     if (decode_mode(*p)) {
         if (launch_tile_table(offsets, p->E, p->C, kDecodeBM, mt, s) != hipSuccess) return MOE_ERR_HIP;
         const DecodeSeg g1 = routed_seg1(*p, x_disp, 0, offsets, mt, w13, s13, h);
-        if (run_decode(&g1, nullptr, nullptr, p->k, nullptr, p->w_dtype, (int64_t)p->T * p->k, s) != hipSuccess) return MOE_ERR_HIP;
+        if (run_decode(&g1, nullptr, nullptr, p->k, nullptr, p->w_dtype, (int64_t)p->T * p->k, -1, s) != hipSuccess) return MOE_ERR_HIP;
         const DecodeSeg g2 = routed_seg2(*p, h, offsets, mt, w2, s2, EPI_STORE, y_disp);
-        return hip_status(run_decode(&g2, nullptr, nullptr, p->k, nullptr, p->w_dtype, (int64_t)p->T * p->k, s));
+        return hip_status(run_decode(&g2, nullptr, nullptr, p->k, nullptr, p->w_dtype, (int64_t)p->T * p->k, -1, s));
     }
     if (launch_tile_table(offsets, p->E, p->C, gemm_bm(*p), mt, s) != hipSuccess) return MOE_ERR_HIP;
     if (run_gemm1(*p, x_disp, offsets, mt, w13, s13, h, s) != hipSuccess) return MOE_ERR_HIP;
@@ -504,9 +508,10 @@ moe_status moe_shared_ffn(const moe_problem* p, const void* x, const void* w13_s
     if (decode_mode(*p)) {
         void* h_sh = at<void>(ws, L.h_sh);
         const DecodeSeg g1 = shared_seg1(*p, x, w13_sh, h_sh);
-        if (run_decode(nullptr, &g1, nullptr, p->k, nullptr, MOE_BF16, (int64_t)p->T * p->k, s) != hipSuccess) return MOE_ERR_HIP;
+        // shared experts: every group holds exactly T rows
+        if (run_decode(nullptr, &g1, nullptr, p->k, nullptr, MOE_BF16, (int64_t)p->T * p->k, p->T, s) != hipSuccess) return MOE_ERR_HIP;
         const DecodeSeg g2 = shared_seg2(*p, h_sh, w2_sh, y_shared);
-        return hip_status(run_decode(nullptr, &g2, nullptr, p->k, nullptr, MOE_BF16, (int64_t)p->T * p->k, s));
+        return hip_status(run_decode(nullptr, &g2, nullptr, p->k, nullptr, MOE_BF16, (int64_t)p->T * p->k, p->T, s));
     }
     return hip_status(run_shared(*p, x, w13_sh, w2_sh, at<void>(ws, L.h_sh), y_shared, s));
 }
@@ -608,12 +613,14 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
         void* h_sh = at<void>(ws, L.h_sh);
         const DecodeSeg r1 = routed_seg1(P, x, 1, offsets, mt, w13, s13, h);
         const DecodeSeg sh1 = P.n_shared ? shared_seg1(P, x, w13_sh, h_sh) : DecodeSeg{};
-        e = run_decode(&r1, P.n_shared ? &sh1 : nullptr, row_src, P.k, w, P.w_dtype, (int64_t)P.T * P.k, s);
+        // rows per group <= T: the dispatch keeps at most one route of a token per
+        // expert (a repeated expert is a malformed route), shared groups hold T
+        e = run_decode(&r1, P.n_shared ? &sh1 : nullptr, row_src, P.k, w, P.w_dtype, (int64_t)P.T * P.k, P.T, s);
         if (e == hipSuccess) e = mark(m, MOE_STAGE_GEMM1, s);
         if (e != hipSuccess) return MOE_ERR_HIP;
         const DecodeSeg r2 = routed_seg2(P, h, offsets, mt, w2, s2, EPI_COMBINE, ybuf);
         const DecodeSeg sh2 = P.n_shared ? shared_seg2(P, h_sh, w2_sh, y_sh) : DecodeSeg{};
-        e = run_decode(&r2, P.n_shared ? &sh2 : nullptr, row_src, P.k, w, P.w_dtype, (int64_t)P.T * P.k, s);
+        e = run_decode(&r2, P.n_shared ? &sh2 : nullptr, row_src, P.k, w, P.w_dtype, (int64_t)P.T * P.k, P.T, s);
         if (e == hipSuccess) e = mark(m, MOE_STAGE_GEMM2, s);
         if (e == hipSuccess) e = mark(m, MOE_STAGE_SHARED, s);
         if (e == hipSuccess)

@@ -128,7 +128,9 @@ struct DecodeArgs {
     int k_top;
     const float* route_w;
 };
-hipError_t launch_decode_gemm(const DecodeArgs& d, int w_dtype, int split, int grid, hipStream_t s);
+// small_m: no group has more than 8 rows (the 8-row staging of the decode ring)
+hipError_t launch_decode_gemm(const DecodeArgs& d, int w_dtype, int split, int small_m, int grid,
+                              hipStream_t s);
 
 // ---- combine -----------------------------------------------------------------
 // out[t] = sum_j (route_dst >= 0) coef * y[src] (+ y_shared[t]); NaN row when a

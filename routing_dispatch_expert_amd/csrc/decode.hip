@@ -23,11 +23,15 @@
 // at a time, each wavefront on a quarter of K; the four partial sums are
 // added in LDS in wavefront order.
 //
-// Loads: each wavefront owns a private ring of kDStages LDS stages (8 KB:
+// Loads: each wavefront owns a private 32 KB LDS ring of stages (4 stages of
 // 32 activation rows and 32 weight rows of 128 bytes) filled by direct
 // global -> LDS loads; it waits only on its own vector-memory counter (no
-// workgroup barrier), so each wavefront keeps (kDStages - 1) x 8 KB in
-// flight.  Within a 64-wide K group, lane half h supplies K elements
+// workgroup barrier), so each wavefront keeps all stages but the one being
+// multiplied in flight.  When no expert can hold more than 8 rows (batches
+// of at most 8 tokens) a stage stages only 8 activation rows (5 KB): the
+// ring then holds 6 stages and keeps 20 KB of weights in flight instead of
+// 12 KB.  Activation rows 8..31 of the MFMA then repeat rows 0..7; their
+// output rows are never stored.  Within a 64-wide K group, lane half h supplies K elements
 // [32h + 8j, 32h + 8j + 8) to MFMA step j (the same permutation of K for both
 // operands leaves the product unchanged), so each lane's bytes for a group
 // are one 64-byte run.  16-byte chunk c of row r sits at chunk slot
@@ -38,9 +42,18 @@ namespace rde {
 namespace {
 
 constexpr int kDWaves = 4;          // wavefronts per workgroup
-constexpr int kDStages = 4;         // LDS ring stages per wavefront
-constexpr int kDStage = 8192;       // bytes per stage: A 4 KB + B 4 KB
+constexpr int kDRing = 32768;       // LDS ring bytes per wavefront
 constexpr int kDGroupK = 64;        // K elements per stage
+
+// Stage layout: AR activation rows then 32 weight rows, 128 bytes each.
+template <bool SMALLM>
+struct DRing {
+    static constexpr int AR = SMALLM ? 8 : 32;        // activation rows staged
+    static constexpr int A_BYTES = AR * 128;
+    static constexpr int STAGE = A_BYTES + 4096;
+    static constexpr int NST = kDRing / STAGE;        // 4 or 6 stages
+    static constexpr int PER = AR / 8 + 4;            // DMA instructions per stage
+};
 
 __device__ __forceinline__ uint32_t lds_addr_d(const void* p) {
     return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
@@ -61,12 +74,18 @@ __device__ __forceinline__ void dma16_d(const void* g, uint32_t lds) {
         : "memory");
 }
 
-// Wait until at most n of this wavefront's vector-memory operations are
-// outstanding (n = 8 x stages issued after the one needed).
-__device__ __forceinline__ void wait_own(int stages_after) {
-    if (stages_after >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if (stages_after == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// Wait until at most PER x n of this wavefront's vector-memory operations are
+// outstanding (n = stages issued after the one needed; PER DMA instructions
+// per stage).
+template <int PER>
+__device__ __forceinline__ void wait_stages(int n) {
+    switch (n) {
+        case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * PER) : "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;   // never less than needed
+    }
 }
 
 // Expert owning tile ti: the largest g with tbl[g] <= ti (tbl non-decreasing,
@@ -178,9 +197,10 @@ struct Item {
 // them over every CU.  Work items exist only for experts
 // with rows (the dispatch's 32-row tile table, kept in LDS with the experts'
 // row ranges).
-template <int EPI0, int EPI1, bool FP8, bool SPLIT>
+template <int EPI0, int EPI1, bool FP8, bool SPLIT, bool SMALLM>
 __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs d) {
-    __shared__ __attribute__((aligned(1024))) unsigned char rings[kDWaves][kDStages * kDStage];
+    using RG = DRing<SMALLM>;
+    __shared__ __attribute__((aligned(1024))) unsigned char rings[kDWaves][kDRing];
     __shared__ float red[SPLIT ? (kDWaves - 1) * 16 * 64 : 1];
     // wave index in a scalar register: the work item, and with it the segment
     // descriptor, is then wave-uniform (scalar loads, no vector-memory wait)
@@ -226,12 +246,14 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
         for (int i = 0; i < 4; ++i) {
             const int r = 8 * i + dr;                 // row within the 32-row block
             const int c = dsl ^ dswz(r);              // logical chunk loaded into slot dsl
-            const int m = min(r, it.mrows - 1);
-            int64_t arow;
-            if (s.offsets == nullptr) arow = (int64_t)(m0 + m);                            // uniform rows
-            else if (s.gather) arow = (int64_t)(d.row_src[it.base + m0 + m] / d.k_top);      // token of the route
-            else arow = (int64_t)(it.base + m0 + m);
-            it.asrc[i] = (const char*)s.A + (arow * s.lda) * 2 + c * 16;
+            if (i < RG::AR / 8) {
+                const int m = min(r, it.mrows - 1);
+                int64_t arow;
+                if (s.offsets == nullptr) arow = (int64_t)(m0 + m);                            // uniform rows
+                else if (s.gather) arow = (int64_t)(d.row_src[it.base + m0 + m] / d.k_top);      // token of the route
+                else arow = (int64_t)(it.base + m0 + m);
+                it.asrc[i] = (const char*)s.A + (arow * s.lda) * 2 + c * 16;
+            }
             int n;
             if ((it.si == 0 ? EPI0 : EPI1) == EPI_SWIGLU) n = r < 16 ? it.blk * 16 + r : s.I + it.blk * 16 + (r - 16);
             else n = min(it.blk * 32 + r, s.N_w - 1);
@@ -275,12 +297,13 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
         const int k0 = (it.g0 + gk) * kDGroupK;
         const int seg = k0 / s.k_seg;
         const int64_t kb = (int64_t)seg * s.b_seg_stride + (k0 - seg * s.k_seg);
-        const uint32_t st = ring0 + slot * kDStage;
+        const uint32_t st = ring0 + slot * RG::STAGE;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16_d(it.asrc[i] + (int64_t)k0 * 2, __builtin_amdgcn_readfirstlane(st + i * 1024));
+        for (int i = 0; i < RG::AR / 8; ++i)
+            dma16_d(it.asrc[i] + (int64_t)k0 * 2, __builtin_amdgcn_readfirstlane(st + i * 1024));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            dma16_d(it.bsrc[i] + kb * (fp8 ? 1 : 2), __builtin_amdgcn_readfirstlane(st + 4096 + i * 1024));
+            dma16_d(it.bsrc[i] + kb * (fp8 ? 1 : 2), __builtin_amdgcn_readfirstlane(st + RG::A_BYTES + i * 1024));
     };
 
     Item cur, nxt;
@@ -290,7 +313,7 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     int pre = 0;                   // stages of `cur` already issued
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     while (true) {
-        for (; pre < min(kDStages - 1, cur.nK); ++pre) issue(cur, pre, (issued++) & (kDStages - 1));
+        for (; pre < min(RG::NST - 1, cur.nK); ++pre) issue(cur, pre, (issued++) % RG::NST);
         const bool has_next = cur.u + stride < total;
         const bool cur_fp8 = FP8 && cur.si == 0;
 
@@ -298,14 +321,15 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
         for (int gk = 0; gk < cur.nK; ++gk) {
-            wait_own(min(kDStages - 2, cur.nK - 1 - gk));
-            const unsigned char* sa = ring + (consumed & (kDStages - 1)) * kDStage;
-            const unsigned char* sb = sa + 4096;
+            wait_stages<RG::PER>(min(RG::NST - 2, cur.nK - 1 - gk));
+            const unsigned char* sa = ring + (consumed % RG::NST) * RG::STAGE;
+            const unsigned char* sb = sa + RG::A_BYTES;
+            const int ra = SMALLM ? (r32 & 7) : r32;   // activation row of this lane's fragment
             bf16x8 af[4], bfr[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int c = 4 * h + j;
-                af[j] = *(const bf16x8*)(sa + r32 * 128 + ((c ^ dswz(r32)) * 16));
+                af[j] = *(const bf16x8*)(sa + ra * 128 + ((c ^ dswz(ra)) * 16));
                 if (cur_fp8) {
                     // 8 e4m3 codes at byte (32h + 8j) of the 64-byte row group
                     const int byte = 32 * h + 8 * j;
@@ -317,8 +341,8 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage read before it is refilled
             ++consumed;
-            const int s3 = gk + kDStages - 1;
-            if (s3 < cur.nK) issue(cur, s3, (issued++) & (kDStages - 1));
+            const int s3 = gk + RG::NST - 1;
+            if (s3 < cur.nK) issue(cur, s3, (issued++) % RG::NST);
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[j], acc, 0, 0, 0);
         }
@@ -358,18 +382,22 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
 
 }  // namespace
 
-hipError_t launch_decode_gemm(const DecodeArgs& d, int w_dtype, int split, int grid, hipStream_t st) {
+hipError_t launch_decode_gemm(const DecodeArgs& d, int w_dtype, int split, int small_m, int grid,
+                              hipStream_t st) {
     const bool fp8 = w_dtype == MOE_E4M3;
     const int e0 = d.seg[0].epi;
     const int e1 = d.n_seg > 1 ? d.seg[1].epi : ((e0 == EPI_SWIGLU || e0 == EPI_RELU2) ? EPI_SWIGLU : EPI_F32);
     dim3 g(grid), b(kDWaves * 64);
-#define RDE_DEC(A, B)                                                                              \
-    if (e0 == A && e1 == B) {                                                                      \
-        if (fp8 && split) hipLaunchKernelGGL((decode_gemm_kernel<A, B, true, true>), g, b, 0, st, d);   \
-        else if (fp8) hipLaunchKernelGGL((decode_gemm_kernel<A, B, true, false>), g, b, 0, st, d);      \
-        else if (split) hipLaunchKernelGGL((decode_gemm_kernel<A, B, false, true>), g, b, 0, st, d);    \
-        else hipLaunchKernelGGL((decode_gemm_kernel<A, B, false, false>), g, b, 0, st, d);              \
-        return hipGetLastError();                                                                  \
+#define RDE_DEC4(A, B, SM)                                                                              \
+    if (fp8 && split) hipLaunchKernelGGL((decode_gemm_kernel<A, B, true, true, SM>), g, b, 0, st, d);   \
+    else if (fp8) hipLaunchKernelGGL((decode_gemm_kernel<A, B, true, false, SM>), g, b, 0, st, d);      \
+    else if (split) hipLaunchKernelGGL((decode_gemm_kernel<A, B, false, true, SM>), g, b, 0, st, d);    \
+    else hipLaunchKernelGGL((decode_gemm_kernel<A, B, false, false, SM>), g, b, 0, st, d);
+#define RDE_DEC(A, B)                      \
+    if (e0 == A && e1 == B) {              \
+        if (small_m) { RDE_DEC4(A, B, true) } \
+        else { RDE_DEC4(A, B, false) }     \
+        return hipGetLastError();          \
     }
     RDE_DEC(EPI_SWIGLU, EPI_SWIGLU)
     RDE_DEC(EPI_RELU2, EPI_SWIGLU)
@@ -377,6 +405,7 @@ hipError_t launch_decode_gemm(const DecodeArgs& d, int w_dtype, int split, int g
     RDE_DEC(EPI_STORE, EPI_F32)
     RDE_DEC(EPI_F32, EPI_F32)
 #undef RDE_DEC
+#undef RDE_DEC4
     return hipErrorInvalidValue;
 }
 
