@@ -26,13 +26,14 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 N_BANKS = 4                  # rotating x / logits banks
+MIN_WARMUP_S = 0.2           # shortest warm-up of a sweep workload
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="prefill_T2048")
     ap.add_argument("--sweep", default="prefill_T256,prefill_T8192,decode_T1,decode_T32,"
                     "relu2_distinct_R16,relu2_shared_R1,sigmoid_T2048",
@@ -70,7 +71,7 @@ def stage_bytes_flops(cs, R, touched, ab, wb):
     return st
 
 
-def run_workload(name, steps, warmup, with_events=True, protocols=False):
+def run_workload(name, steps, warmup, with_events=True, protocols=False, min_warmup_s=0.0):
     import torch
     import routing_dispatch_expert_amd as rde
     import synth
@@ -107,8 +108,16 @@ def run_workload(name, steps, warmup, with_events=True, protocols=False):
         rde.moe_forward(p, x, lg, base.score_bias, None, None, base.w13, base.w2, base.s13, base.s2,
                         base.w13_sh, base.w2_sh, out, meta, ws)
 
-    for i in range(warmup):
+    # `warmup` steps, continued until min_warmup_s has passed (the short sweep
+    # workloads: a layer of a few tens of microseconds then also starts at full
+    # clocks)
+    tw = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - tw < min_warmup_s:
         step(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     # timed region 1: plain steps (the throughput figure)
     t0 = time.perf_counter()
@@ -240,7 +249,62 @@ def roofline_of(res, stage):
             "us": round(us, 2), "alg_bytes": byts, "alg_flops": flops}
 
 
-def summary(res):
+def layer_work(cs, R, touched):
+    """Algorithmic bytes and flops of the whole layer, counted as the method
+    moves them: the non-empty experts' weights (and the shared experts'), the
+    logits and route metadata, x read once, the expert-contiguous row copy and
+    the intermediate h each written and read once, and out written."""
+    T, H, E, k, I = cs.T, cs.H, cs.E, cs.k, cs.I
+    ab = 4 if cs.act_fmt == 0 else 2
+    wb = {0: 4, 1: 2, 2: 1}[cs.w_fmt]
+    n_w = 2 * I if cs.act == 0 else I
+    sc = 4 * (n_w + H) if cs.w_fmt == 2 else 0
+    byts = touched * ((n_w + I) * H * wb + sc)
+    byts += T * E * 4 + T * k * 16 + T * H * ab + 2 * R * H * ab + 2 * R * I * ab + T * H * ab
+    flops = 2 * R * H * (n_w + I) + 2 * R * H
+    if cs.n_shared:
+        Is, S = cs.I_shared, cs.n_shared
+        byts += S * 3 * Is * H * 2
+        flops += S * 2 * T * H * 3 * Is
+    return byts, flops
+
+
+def layer_roofline(res, copy_gbps=None):
+    """t_roofline / t_measured for the whole layer, t_roofline = max(bytes /
+    HBM peak, flops / bf16 MFMA peak); `frac_copy` takes the measured device
+    copy bandwidth in place of the HBM peak."""
+    byts, flops = layer_work(res["cs"], res["R"], res["touched"])
+    t_meas = res["wall"] / res["steps"]
+    t_h, t_m = byts / (HBM_PEAK_GBPS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
+    out = {"alg_bytes": byts, "alg_flops": flops, "t_hbm_us": round(t_h * 1e6, 2),
+           "t_mfma_us": round(t_m * 1e6, 2), "bound": "mfma" if t_m > t_h else "hbm",
+           "t_roofline_us": round(max(t_h, t_m) * 1e6, 2),
+           "frac": round(max(t_h, t_m) / t_meas, 4)}
+    if copy_gbps:
+        t_hc = byts / (copy_gbps * 1e9)
+        out["frac_copy"] = round(max(t_hc, t_m) / t_meas, 4)
+    return out
+
+
+def measure_copy_gbps(torch, mib=1024, reps=5):
+    """Device-to-device copy of `mib` MiB: bytes read + written per second."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return round(2 * n / sec / 1e9, 1)
+
+
+def summary(res, copy_gbps=None):
     cs, st, bf = res["cs"], res["stages"], res["bf"]
     disp_us = st["count"] + st["scatter"]
     disp_b = bf["count"][0] + bf["scatter"][0]
@@ -256,6 +320,7 @@ def summary(res):
         "stages_us": {k: round(v, 2) for k, v in st.items()},
         "ms_per_step_with_stage_events": round(res["wall_ev"] / res["steps"] * 1e3, 4)
         if res.get("wall_ev") else None,
+        "layer_roofline": layer_roofline(res, copy_gbps),
     }
 
 
@@ -276,7 +341,18 @@ def cpu_baseline(res, n_tokens):
     r = oracle.forward(sub, x, lg, w13, w2, conv(base.s13), conv(base.s2), conv(base.w13_sh),
                        conv(base.w2_sh), score_bias=conv(base.score_bias))
     sec = r["seconds"]
+    try:
+        host_cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        host_cores = os.cpu_count()
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(n_tokens / sec, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "host_cores": host_cores, "cpu_model": model,
             "sample": f"first {n_tokens} of {cs.T} tokens of {cs.name}: routing, count-first "
                       f"dispatch, expert FFN and combine for them ({sec:.1f} s)",
             "us_per_layer_extrapolated": round(sec / n_tokens * cs.T * 1e6, 1)}
@@ -301,9 +377,10 @@ def main():
     print(f"[bench] workload {args.workload}: warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
     res = run_workload(args.workload, args.steps, args.warmup, protocols=bool(args.protocols))
+    copy_gbps = measure_copy_gbps(torch) if args.protocols else None
     cs = res["cs"]
     ms = res["wall"] / args.steps * 1e3
-    summ = summary(res)
+    summ = summary(res, copy_gbps)
     dom = dominant_gemm(res)
     line = {
         "metric": "MoE layer tokens/s + us/layer; dispatch HBM GB/s, grouped-GEMM MFMA % of peak",
@@ -320,6 +397,7 @@ def main():
                    "n_shared": cs.n_shared, "parallelism": "none (1 GPU)"},
         **summ,
         "roofline": roofline_of(res, dom),
+        "copy_GBps": copy_gbps,
     }
     if res.get("protocols"):
         pr = dict(res["protocols"])
@@ -335,9 +413,9 @@ def main():
     sweep = {}
     for name in [s for s in args.sweep.split(",") if s]:
         print(f"[bench] sweep {name}", file=sys.stderr, flush=True)
-        r2 = run_workload(name, max(5, args.steps // 3), 10)
+        r2 = run_workload(name, max(5, args.steps // 3), 10, min_warmup_s=MIN_WARMUP_S)
         ms2 = r2["wall"] / max(5, args.steps // 3) * 1e3
-        sw = summary(r2)
+        sw = summary(r2, copy_gbps)
         sw["tokens_per_s"] = round(r2["cs"].T / (ms2 * 1e-3), 1)
         sw["ms_per_step"] = round(ms2, 4)
         d2 = dominant_gemm(r2)
