@@ -1,0 +1,51 @@
+"""Host-side checks of bench.py: the whole-layer work accounting against the
+algorithmic bytes and flops of the workload table (count-first MoE layer:
+weights of the touched and shared experts, logits, route metadata, x once,
+row copy and h written and read, out written), and the one-GPU guard."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import synth  # noqa: E402
+
+
+# (workload, kept rows R, touched experts, GB, GFLOP) of the seed-0 workloads
+TABLE = [
+    ("prefill_T256", 2048, 128, 1.638, 25.8),
+    ("prefill_T2048", 16384, 128, 1.830, 206.2),
+    ("prefill_T8192", 65536, 128, 2.488, 824.9),
+    ("decode_T1", 6, 6, 0.139, 0.1),
+    ("relu2_shared_R1", 9, 9, 0.057, 0.1),
+    ("relu2_distinct_R16", 144, 144, 0.908, 0.9),
+]
+
+
+@pytest.mark.parametrize("name,R,touched,gb,gflop", TABLE)
+def test_layer_work_matches_table(name, R, touched, gb, gflop):
+    byts, flops = bench.layer_work(synth.case(name), R, touched)
+    assert round(byts / 1e9, 3) == pytest.approx(gb, abs=1e-3)
+    assert round(flops / 1e9, 1) == pytest.approx(gflop, abs=0.1)
+
+
+def test_layer_roofline_bound_and_fraction():
+    res = {"cs": synth.case("prefill_T8192"), "R": 65536, "touched": 128,
+           "wall": 2 * 1.0e-3, "steps": 2}
+    lr = bench.layer_roofline(res, copy_gbps=4000.0)
+    assert lr["bound"] == "mfma"                      # 824.9 GFLOP > 2.488 GB at the ridge
+    assert lr["t_roofline_us"] == pytest.approx(329.96, abs=0.01)
+    assert lr["frac"] == pytest.approx(0.32996, abs=1e-4)
+    # at 4 TB/s the byte term (622 us) exceeds the flop term
+    assert lr["frac_copy"] == pytest.approx(2.488270848e9 / 4e12 / 1e-3, abs=1e-3)
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
