@@ -126,6 +126,21 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
         : "memory");
 }
 
+// The same for 4 bytes per lane (global_load_lds_dword): lane l's dword
+// lands at `lds` + 4*l.
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(lds)
+        : "memory");
+}
+
 // Wait until at most N of this thread's vector-memory operations are
 // outstanding, then workgroup barrier.  No memory fence: LDS written by
 // global_load_lds is complete once the issuing thread's vmcnt has dropped
@@ -187,6 +202,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char sB[kStages][B_STAGE];
     __shared__ int32_t s_mt[kMaxGroupsLds + 1], s_off[kMaxGroupsLds + 1];
     __shared__ __attribute__((aligned(16))) unsigned char sOut[NW][32 * kOutPitch];
+    // EPI_COMBINE: the tile's routes and their weights, loaded during the
+    // k-loop by direct-to-LDS loads (plain loads in the epilogue would wait
+    // for every k-tile of the next tile already in flight)
+    __shared__ int32_t s_rq[EPI == EPI_COMBINE ? BM : 1];
+    __shared__ float s_rw[EPI == EPI_COMBINE ? BM : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -227,6 +247,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
 
     // wave-uniform LDS bases of this wave's DMA blocks in ring slot 0
     const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(sA[0]) + wave * 1024);
+    const uint32_t rq0 = __builtin_amdgcn_readfirstlane(lds_addr(s_rq) + wave * 256);
+    const uint32_t rw0 = __builtin_amdgcn_readfirstlane(lds_addr(s_rw) + wave * 256);
+    // routes of the epilogue staged in LDS: needs k-tiles 1, 5 and 9 (see the k-loop)
+    const bool route_pf = EPI == EPI_COMBINE && a.K / BK >= 10;
     const uint32_t lb0 = __builtin_amdgcn_readfirstlane(lds_addr(sB[0]) + wave * LB * 1024);
 
     // A tile's place in the problem and this thread's DMA sources (byte
@@ -374,6 +398,18 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
                 const int s = kt + kStages - 1;
                 if (s < nk) issue(cur, s, (sbase + s) & (kStages - 1));
                 else if (has_next) issue(nxt, s - nk, (sbase + s) & (kStages - 1));
+                if (EPI == EPI_COMBINE && route_pf && wave < 4) {
+                    // waves 0..3 stage the routes of tile rows 64 wave + lane at
+                    // k-tile 1 (every wave has left the previous tile's
+                    // epilogue), then their weights at k-tile 5 (the routes
+                    // were loaded before k-tile 5 was, so they have landed);
+                    // the weights have landed by the barrier of k-tile 9
+                    if (kt == 1) {
+                        dma4(a.row_src + a_row0 + min(64 * wave + lane, rows - 1), rq0);
+                    } else if (kt == 5) {
+                        dma4(a.route_w + s_rq[64 * wave + lane], rw0);
+                    }
+                }
                 if (NA == 0) continue;
                 const int slot = (sbase + kt) & (kStages - 1);
                 const unsigned char* sa = sA[slot];
@@ -455,8 +491,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
             float cw = 1.0f;
             int32_t q = 0;
             if (EPI == EPI_COMBINE) {
-                q = a.row_src[orow];
-                cw = a.route_w[q];
+                if (route_pf) {
+                    q = s_rq[min(row, rows - 1)];
+                    cw = s_rw[min(row, rows - 1)];
+                } else {
+                    q = a.row_src[orow];
+                    cw = a.route_w[q];
+                }
             }
             // SwiGLU: gate block nb pairs with up block nb + NBW/2
             constexpr int NB = EPI == EPI_SWIGLU ? NBW / 2 : NBW;
