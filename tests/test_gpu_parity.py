@@ -37,6 +37,9 @@ SMALL = {
     # hidden / intermediate not multiples of the 256-column tile
     "ragged_n_relu2": ("relu2_distinct_R8", dict(H=384, I=384)),
     "ragged_n_swiglu": ("prefill_T256", dict(T=300, H=384, E=4, k=2, I=384, C=300)),
+    # down projection with K >= 320 (the combine epilogue's routes staged in LDS)
+    # over two m-tiles per expert, the second ragged
+    "multi_tile_k384": ("prefill_T256", dict(T=600, H=256, E=4, k=2, I=384, C=600)),
     # decode-shaped (few rows per expert): slot-indexed expert GEMMs
     "decode_fp8": ("skewed_fp8", dict(T=16, H=256, E=32, k=4, I=256, C=16)),
     "decode_rows_over_32": ("skewed_bf16", dict(T=180, H=256, E=32, k=2, I=128, C=180)),
