@@ -18,7 +18,8 @@
 // Kernel 2, scatter: one block per token.  Each route's final rank is
 // base[block][e] + its in-block rank; a rank below C places the route at row
 // offsets[e] + rank.  The token's row is read once and stored to each of its
-// kept rows with 16-byte vector stores.
+// kept rows with 16-byte vector stores.  When no row copy is asked for, a
+// metadata-only variant takes one thread per route.
 #include <algorithm>
 #include <type_traits>
 
@@ -261,6 +262,29 @@ __global__ __launch_bounds__(256) void scatter_kernel(
             if (row >= 0) x_disp[(int64_t)row * H_vec + c] = v;
         }
     }
+}
+
+// Metadata only (the expert GEMMs read x in place): one thread per route.
+__global__ __launch_bounds__(256) void scatter_meta_kernel(
+    int64_t Q, int E, int C, int64_t r_max, const int32_t* __restrict__ rexp,
+    const int32_t* __restrict__ lrank, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ route_dst,
+    int32_t* __restrict__ row_src) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid < Q) {
+        const int e = rexp[gid];
+        int32_t row;
+        if (e < 0) {
+            row = -2;
+        } else {
+            const int32_t r = base[(gid / kCountBlock) * E + e] + lrank[gid];
+            row = r < C ? offsets[e] + r : -1;
+            if (row >= 0) row_src[row] = (int32_t)gid;
+        }
+        route_dst[gid] = row;
+    }
+    // rows R .. r_max-1 of row_src are unused: -1
+    for (int64_t r = offsets[E] + gid; r < r_max; r += (int64_t)gridDim.x * blockDim.x) row_src[r] = -1;
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
@@ -512,6 +536,12 @@ hipError_t launch_scatter(const void* x, int T, int H, int k, int E, int C, int 
                           const int32_t* base, const int32_t* offsets, int32_t* route_dst,
                           int32_t* row_src, void* x_disp, hipStream_t s) {
     if (T == 0) return hipSuccess;
+    if (x_disp == nullptr) {
+        const int64_t Q = (int64_t)T * k;
+        hipLaunchKernelGGL(scatter_meta_kernel, dim3((unsigned)((Q + 255) / 256)), dim3(256), 0, s, Q, E, C,
+                           r_max, rexp, lrank, base, offsets, route_dst, row_src);
+        return hipGetLastError();
+    }
     const int H_vec = (int)((int64_t)H * elem_bytes / 16);  // H*elem_bytes is a multiple of 256
     hipLaunchKernelGGL(scatter_kernel<uint4>, dim3(T), dim3(256), 0, s, (const uint4*)x, H_vec, k, E,
                        C, r_max, rexp, lrank, base, offsets, route_dst, row_src, (uint4*)x_disp);
