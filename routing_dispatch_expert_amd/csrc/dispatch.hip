@@ -11,9 +11,11 @@
 // the group size.  Per-wave counts are then prefix-summed over the block's
 // waves (giving the rank of a route among the block's routes of its expert)
 // and the block totals are published (write-through stores).  The last
-// block to arrive (atomic ticket) turns the per-block totals into per-block bases, writes the raw
-// counts, the exclusive scan of min(count, C) and the m-tile table of the
-// grouped GEMM, and resets the ticket.
+// block to arrive (atomic ticket) turns the per-block totals into per-block
+// bases, writes the raw counts, the exclusive scan of min(count, C) and the
+// m-tile table of the grouped GEMM, and resets the ticket.  A launch of one
+// block (at most 2048 routes) keeps its totals in registers and takes no
+// ticket.
 //
 // Kernel 2, scatter: one block per token.  Each route's final rank is
 // base[block][e] + its in-block rank; a rank below C places the route at row
@@ -30,11 +32,60 @@ namespace {
 
 constexpr int kScanThreads = 256;
 
+// Inclusive prefix sum over the 64 lanes of a wavefront: a Kogge-Stone scan
+// inside each row of 16 lanes by DPP row shifts (lanes shifted in from
+// outside the row read 0), then the totals of the lower rows.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t x, int lane) {
+    x += (int32_t)__builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += (int32_t)__builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += (int32_t)__builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += (int32_t)__builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    const int32_t r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+                  r2 = __builtin_amdgcn_readlane(x, 47);
+    if (lane >= 16) x += r0;
+    if (lane >= 32) x += r1;
+    if (lane >= 48) x += r2;
+    return x;
+}
+
 // Block-wide exclusive scan of up to kScanThreads * per-thread values held in
 // LDS array `v` (n entries, in place); returns the total.  Two arrays at once.
+// Called by all kScanThreads threads of the block.
 __device__ void block_scan2(int32_t* a, int32_t* b, int n, int32_t* tot_a, int32_t* tot_b) {
     __shared__ int32_t sa[kScanThreads], sb[kScanThreads];
     const int tid = threadIdx.x;
+    if (n <= kScanThreads) {
+        // one value per thread: wavefront scans, then the wavefront totals
+        constexpr int NWV = kScanThreads / kWave;
+        const int lane = tid & (kWave - 1), wv = tid / kWave;
+        const int32_t va = tid < n ? a[tid] : 0, vb = tid < n ? b[tid] : 0;
+        const int32_t ia = wave_incl_scan(va, lane), ib = wave_incl_scan(vb, lane);
+        if (lane == kWave - 1) {
+            sa[wv] = ia;
+            sb[wv] = ib;
+        }
+        __syncthreads();
+        int32_t pa = 0, pb = 0, ta = 0, tb = 0;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) {
+            if (w < wv) {
+                pa += sa[w];
+                pb += sb[w];
+            }
+            ta += sa[w];
+            tb += sb[w];
+        }
+        if (tid < n) {
+            a[tid] = pa + ia - va;
+            b[tid] = pb + ib - vb;
+        }
+        if (tid == 0) {
+            *tot_a = ta;
+            *tot_b = tb;
+        }
+        __syncthreads();
+        return;
+    }
     const int per = (n + kScanThreads - 1) / kScanThreads;
     const int lo = tid * per, hi = min(n, lo + per);
     int32_t ra = 0, rb = 0;
@@ -137,22 +188,59 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
     const int wave_bad = wave_sum_i32(n_bad);
     if (badm && lane == 0) atomicAdd(&ctrl[CTRL_BAD_ROUTES], wave_bad);
     __syncthreads();
-    for (int e = tid; e < E; e += blockDim.x) {
+    // one block (at most kCountBlock routes): its totals are the counts and no
+    // other block takes part, so they stay in registers
+    constexpr int kMaxEPerThread = 4;
+    const bool single = gridDim.x == 1 && E <= kMaxEPerThread * (int)blockDim.x;
+    int32_t tot[kMaxEPerThread];
+    for (int i = 0, e = tid; e < E; ++i, e += blockDim.x) {
         int32_t run = 0;
         for (int w = 0; w < kCountWaves; ++w) {
             const int32_t c = lds[w * E + e];
             lds[w * E + e] = run;
             run += c;
         }
-        // write-through to the device-coherent level: the last block reads it
-        __hip_atomic_store(&partial[(int64_t)blockIdx.x * E + e], run, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        if (single) {
+            if (i < kMaxEPerThread) tot[i] = run;
+        } else {
+            // write-through to the device-coherent level: the last block reads it
+            __hip_atomic_store(&partial[(int64_t)blockIdx.x * E + e], run, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < kCountPerLane; ++it) {
         const int64_t q = q0 + it * kWave + lane;
         if (q < Q) lrank[q] = ex[it] >= 0 ? hist[ex[it]] + rank_w[it] : -1;
+    }
+
+    int32_t* kept = lds;
+    int32_t* tiles = lds + E;
+    // offsets and the m-tile table from kept[] / tiles[] (all threads)
+    auto finish = [&]() {
+        __syncthreads();
+        block_scan2(kept, tiles, E, &s_tot[0], &s_tot[1]);
+        for (int e = tid; e < E; e += blockDim.x) {
+            offsets[e] = kept[e];
+            mt_off[e] = tiles[e];
+        }
+        if (tid == 0) {
+            offsets[E] = s_tot[0];
+            mt_off[E] = s_tot[1];
+        }
+    };
+    if (single) {
+        __syncthreads();   // every thread is done reading the histograms
+        for (int i = 0, e = tid; e < E; ++i, e += blockDim.x) {
+            partial[e] = 0;   // the only block's base
+            counts[e] = tot[i];
+            const int32_t kp = tot[i] < C ? tot[i] : C;
+            kept[e] = kp;
+            tiles[e] = (kp + bm - 1) / bm;
+        }
+        finish();
+        return;
     }
 
     // ---- last block: per-block bases, counts, offsets, m-tile table ----
@@ -170,8 +258,6 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
                                          __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1);
     __syncthreads();
     if (!s_last) return;
-    int32_t* kept = lds;
-    int32_t* tiles = lds + E;
     const int nb = gridDim.x;
     for (int e = tid; e < E; e += blockDim.x) {
         int32_t run = 0;
@@ -195,17 +281,8 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
         kept[e] = kp;
         tiles[e] = (kp + bm - 1) / bm;
     }
-    __syncthreads();
-    block_scan2(kept, tiles, E, &s_tot[0], &s_tot[1]);
-    for (int e = tid; e < E; e += blockDim.x) {
-        offsets[e] = kept[e];
-        mt_off[e] = tiles[e];
-    }
-    if (tid == 0) {
-        offsets[E] = s_tot[0];
-        mt_off[E] = s_tot[1];
-        ctrl[CTRL_TICKET] = 0;
-    }
+    finish();
+    if (tid == 0) ctrl[CTRL_TICKET] = 0;
 }
 
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets, int E,
