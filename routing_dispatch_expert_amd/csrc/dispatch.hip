@@ -395,21 +395,11 @@ constexpr int kSmallSteps = 2;                            // 64-route steps per 
 // returns the thread's exclusive prefix and writes the total to *tot.
 __device__ int32_t block_exclusive_scan_1024(int32_t v, int32_t* s_wsum, int32_t* tot) {
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-    int32_t x = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int32_t y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-    }
+    const int32_t x = wave_incl_scan(v, lane);
     if (lane == kWave - 1) s_wsum[wv] = x;
     __syncthreads();
     if (wv == 0) {
-        int32_t u = lane < kSmallWaves ? s_wsum[lane] : 0;
-#pragma unroll
-        for (int off = 1; off < kSmallWaves; off <<= 1) {
-            const int32_t y = __shfl_up(u, off, kWave);
-            if (lane >= off) u += y;
-        }
+        const int32_t u = wave_incl_scan(lane < kSmallWaves ? s_wsum[lane] : 0, lane);
         if (lane < kSmallWaves) s_wsum[lane] = u;   // inclusive over waves
     }
     __syncthreads();
