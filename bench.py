@@ -35,9 +35,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="prefill_T2048")
-    ap.add_argument("--sweep", default="prefill_T256,prefill_T8192,decode_T1,decode_T32,"
-                    "relu2_distinct_R16,relu2_shared_R1,sigmoid_T2048",
+    ap.add_argument("--sweep", default="prefill_T256,prefill_T8192,decode_T1,decode_T8,"
+                    "decode_T32,relu2_distinct_R16,relu2_shared_R1,sigmoid_T2048,skewed_bf16,"
+                    "skewed_fp8",
                     help="comma-separated extra workloads timed briefly ('' = none)")
+    ap.add_argument("--dispatch", default="prefill_T2048,prefill_T8192,skewed_bf16",
+                    help="comma-separated workloads whose moe_route / moe_dispatch (with the "
+                         "x_disp row copy) are timed on their own ('' = none)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
     ap.add_argument("--protocols", type=int, default=1,
@@ -48,8 +52,11 @@ def parse():
 
 
 def stage_bytes_flops(cs, R, touched, ab, wb):
-    """Algorithmic bytes and flops of each stage for a batch with R kept
-    rows and `touched` non-empty experts."""
+    """Algorithmic bytes and flops of each stage of moe_forward for a batch
+    with R kept rows and `touched` non-empty experts.  The forward copies
+    token rows into the expert-contiguous buffer only for float32 layers;
+    bf16 layers place routes only (the expert GEMM reads x in place), so
+    their scatter moves route metadata alone."""
     T, H, E, k, I = cs.T, cs.H, cs.E, cs.k, cs.I
     Q = T * k
     r_max = min(Q, E * cs.C)
@@ -58,7 +65,7 @@ def stage_bytes_flops(cs, R, touched, ab, wb):
     st = {
         "route": (T * E * 4 + Q * 8, 0),
         "count": (Q * 4 + Q * 8 + E * 8, 0),
-        "scatter": (T * H * ab + R * H * ab + Q * 16 + r_max * 4, 0),
+        "scatter": ((T * H * ab + R * H * ab if ab == 4 else 0) + Q * 16 + r_max * 4, 0),
         "gemm1": (touched * n_w * (H * wb + sc) + R * H * ab + R * I * ab, 2 * R * H * n_w),
         "gemm2": (touched * H * (I * wb + sc) + R * I * ab + R * H * ab + R * 8, 2 * R * I * H),
         "shared": (0, 0),
@@ -151,6 +158,94 @@ def run_workload(name, steps, warmup, with_events=True, protocols=False, min_war
     wb = {synth.FMT_F32: 4, synth.FMT_BF16: 2, synth.FMT_E4M3: 1}[cs.w_fmt]
     return dict(cs=cs, steps=steps, wall=wall, wall_ev=wall_ev, stages=stages, R=R, touched=touched,
                 bf=stage_bytes_flops(cs, R, touched, ab, wb), base=base, protocols=proto)
+
+
+def dispatch_bytes(cs, R):
+    """Algorithmic bytes of moe_route and of moe_dispatch with the row copy:
+    route reads the logits and writes ids and weights; dispatch reads the
+    ids, writes counts, offsets, route_dst and row_src, reads every token
+    row once and writes one copy per kept route."""
+    import synth
+    T, H, E, k = cs.T, cs.H, cs.E, cs.k
+    ab = 4 if cs.act_fmt == synth.FMT_F32 else 2
+    Q = T * k
+    route = T * E * 4 + Q * 8
+    disp = Q * 4 + E * 4 + (E + 1) * 4 + Q * 4 + cs.r_max * 4 + T * H * ab + R * H * ab
+    return route, disp
+
+
+def measure_dispatch(name, calls=50, min_warmup_s=MIN_WARMUP_S):
+    """moe_route and moe_dispatch (x_disp rows written) called on their own,
+    over four rotating input banks, each call timed with events on the
+    stream it runs on: the count-first dispatch as a standalone data move."""
+    import torch
+    import routing_dispatch_expert_amd as rde
+    import synth
+
+    dev = "cuda:0"
+    cs = synth.case(name)
+    p = rde.make_problem(cs.T, cs.H, cs.E, cs.k, cs.I, cs.C, cs.n_shared, cs.I_shared,
+                         act_dtype=cs.act_fmt, w_dtype=cs.w_fmt, act=cs.act,
+                         renormalize=cs.renormalize, score_func=cs.score_func,
+                         route_scale=cs.route_scale)
+    ws = torch.empty(rde.moe_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    rde.moe_workspace_init(ws)
+    adt = torch.float32 if cs.act_fmt == synth.FMT_F32 else torch.bfloat16
+    banks = []
+    for b in range(N_BANKS):
+        cb = synth.replace(cs, seed=cs.seed + 1000 * b)
+        banks.append(dict(x=synth.make_x(cb, dev), lg=synth.make_logits(cb, dev),
+                          bias=synth.make_score_bias(cb, dev),
+                          ids=torch.empty((cs.T, cs.k), dtype=torch.int32, device=dev),
+                          w=torch.empty((cs.T, cs.k), dtype=torch.float32, device=dev)))
+    counts = torch.empty(cs.E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(cs.E + 1, dtype=torch.int32, device=dev)
+    row_src = torch.empty(cs.r_max, dtype=torch.int32, device=dev)
+    route_dst = torch.empty((cs.T, cs.k), dtype=torch.int32, device=dev)
+    x_disp = torch.empty((cs.r_max, cs.H), dtype=adt, device=dev)
+
+    def route(i):
+        b = banks[i % N_BANKS]
+        rde.moe_route(p, b["lg"], b["bias"], b["ids"], b["w"], ws)
+
+    def disp(i):
+        b = banks[i % N_BANKS]
+        rde.moe_dispatch(p, b["x"], b["ids"], counts, offsets, row_src, route_dst, x_disp, ws)
+
+    for i in range(N_BANKS):
+        route(i)
+    tw = time.perf_counter()
+    i = 0
+    while time.perf_counter() - tw < min_warmup_s:
+        route(i)
+        disp(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    out = {}
+    for label, fn in (("route", route), ("dispatch", disp)):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
+        for i in range(calls):
+            ev[i].record()
+            fn(i)
+        ev[calls].record()
+        torch.cuda.synchronize()
+        d = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(calls))
+        out[label] = d[len(d) // 2]
+    # the last call's realised kept rows (outside the timed region)
+    R = int(offsets[-1].item())
+    if rde.moe_error(ws) != 0:
+        raise RuntimeError("malformed routes reported on synthetic inputs")
+    rb, db = dispatch_bytes(cs, R)
+    gbps = db / (out["dispatch"] * 1e-6) / 1e9
+    return {"calls": "moe_dispatch: count + scan, then route placement and the x_disp row "
+                     "copy; median of %d back-to-back calls" % calls,
+            "T": cs.T, "H": cs.H, "E": cs.E, "k": cs.k, "kept_rows": R,
+            "dispatch_us": round(out["dispatch"], 2), "dispatch_alg_bytes": db,
+            "dispatch_GBps": round(gbps, 1), "dispatch_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "route_us": round(out["route"], 2), "route_alg_bytes": rb,
+            "route_GBps": round(rb / (out["route"] * 1e-6) / 1e9, 1)}
 
 
 def measure_protocols(step, torch, groups=15, calls=20, graph_calls=64, graph_replays=10):
@@ -313,7 +408,8 @@ def summary(res, copy_gbps=None):
     return {
         "us_per_layer": round(res["wall"] / res["steps"] * 1e6, 2),
         "sum_of_stage_us": round(sum(st.values()), 2),
-        "dispatch_GBps": round(disp_b / (disp_us * 1e-6) / 1e9, 1),
+        "dispatch_us": round(disp_us, 2),
+        "dispatch_bytes": disp_b,
         "gemm_mfma_pct": round(100 * g_fl / (g_us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 2),
         "gemm_hbm_GBps": round((bf["gemm1"][0] + bf["gemm2"][0]) / (g_us * 1e-6) / 1e9, 1),
         "kept_rows": res["R"], "experts_touched": res["touched"],
@@ -425,6 +521,16 @@ def main():
         torch.cuda.empty_cache()
     if sweep:
         line["sweep"] = sweep
+    disp = {}
+    for name in [s for s in args.dispatch.split(",") if s]:
+        print(f"[bench] dispatch {name}", file=sys.stderr, flush=True)
+        disp[name] = measure_dispatch(name)
+        torch.cuda.empty_cache()
+    if disp:
+        line["dispatch"] = disp
+        main_d = disp.get(cs.name)
+        if main_d is not None:
+            line["dispatch_GBps"] = main_d["dispatch_GBps"]
     print(json.dumps(line), flush=True)
 
 

@@ -32,8 +32,7 @@ __device__ __forceinline__ void store8(__bf16* p, const float* v) {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const __bf16 a = (__bf16)v[2 * i], b = (__bf16)v[2 * i + 1];
-        w[i] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+        w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
     }
     *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
 }

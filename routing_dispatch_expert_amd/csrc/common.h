@@ -15,6 +15,30 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kWave = 64;
 
+// Two floats -> two bf16 (round to nearest even) in one packed dword, low
+// half first: a single v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// 8 OCP e4m3 codes (two dwords, lowest byte first) -> 8 bf16, exact: every
+// e4m3 value is a bf16 value.  gfx950 converts a pair of e4m3 codes straight
+// to a pair of bf16 (v_cvt_scalef32_pk_bf16_fp8; the scale 1.0 leaves the
+// values unchanged), 4 instructions for 8 weights.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint2 v) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+    const uint4 u = make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                               __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+    return __builtin_bit_cast(bf16x8, u);
+}
+
 // ---- workspace control words (first 256 bytes of ws) --------------------
 enum CtrlWord {
     CTRL_BAD_ROUTES = 0,   // malformed routes seen since the last moe_error

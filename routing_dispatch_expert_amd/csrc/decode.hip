@@ -106,20 +106,6 @@ __device__ __forceinline__ float silu_mul_d(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-    const __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-}
-
-__device__ __forceinline__ bf16x8 e4m3x8_bf16(uint2 v) {
-    typedef float __attribute__((ext_vector_type(2))) f2;
-    const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false);
-    const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true);
-    const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false);
-    const f2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
-    const uint4 u = make_uint4(pack2(a.x, a.y), pack2(b.x, b.y), pack2(c.x, c.y), pack2(d.x, d.y));
-    return __builtin_bit_cast(bf16x8, u);
-}
 
 // Epilogue of one work item: lane holds activation row m = lane % 32 and the
 // weight rows n = 8*(r/4) + 4*(lane/32) + r%4 of acc register r.
@@ -147,7 +133,7 @@ __device__ __forceinline__ void epilogue(const DecodeSeg& s, int group, int blk,
                 }
                 hv[j] = silu_mul_d(gv, uv);
             }
-            *(uint2*)(o + col) = make_uint2(pack2(hv[0], hv[1]), pack2(hv[2], hv[3]));
+            *(uint2*)(o + col) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
         }
         return;
     }
@@ -168,7 +154,7 @@ __device__ __forceinline__ void epilogue(const DecodeSeg& s, int group, int blk,
             *(float4*)((float*)s.out + drow * s.ldo + col) = make_float4(v[0], v[1], v[2], v[3]);
         } else {
             const int64_t oc = (EPI == EPI_RELU2) ? (int64_t)group * s.out_col_per_group + col : col;
-            *(uint2*)((__bf16*)s.out + drow * s.ldo + oc) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+            *(uint2*)((__bf16*)s.out + drow * s.ldo + oc) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
     }
 }
@@ -334,7 +320,7 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
                     // 8 e4m3 codes at byte (32h + 8j) of the 64-byte row group
                     const int byte = 32 * h + 8 * j;
                     const int cc = byte >> 4;
-                    bfr[j] = e4m3x8_bf16(*(const uint2*)(sb + r32 * 128 + ((cc ^ dswz(r32)) * 16) + (byte & 15)));
+                    bfr[j] = e4m3x8_to_bf16x8(*(const uint2*)(sb + r32 * 128 + ((cc ^ dswz(r32)) * 16) + (byte & 15)));
                 } else {
                     bfr[j] = *(const bf16x8*)(sb + r32 * 128 + ((c ^ dswz(r32)) * 16));
                 }

@@ -33,9 +33,13 @@
 // so acc[.][0] and acc[.][1] hold g and u of identical (row, column); a
 // 256-row B tile yields 128 output columns.
 //
-// e4m3 weights are widened to bf16 exactly while being staged into LDS (the
-// hardware converts OCP e4m3 to float32; every e4m3 value is a bf16 value)
-// and the per-row scale multiplies the float32 accumulator.
+// e4m3 weights stay e4m3 in LDS and are widened to bf16 exactly when a
+// fragment is read (the hardware converts OCP e4m3 to float32; every e4m3
+// value is a bf16 value); the per-row scale multiplies the float32
+// accumulator.  Their k-tiles are 64 wide, so that a weight row still
+// arrives in 64-byte pieces and a tile takes half as many k-tiles: the ring
+// then has 3 stages of 48 KB, and the epilogue's output patch borrows the
+// ring slot of the k-tile just multiplied.
 #include <type_traits>
 
 #include "common.h"
@@ -61,18 +65,6 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    const __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-}
-
-// 4 e4m3 codes (one dword) -> 4 bf16 (two dwords), exact.
-__device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
-    typedef float __attribute__((ext_vector_type(2))) f2;
-    const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-    const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-    return make_uint2(pack_bf16x2(lo.x, lo.y), pack_bf16x2(hi.x, hi.y));
-}
 
 // ---- bf16 MFMA kernel --------------------------------------------------------
 // Block tile BM x BN x BK = 256 x 256 x 32, 8 waves, a ring of kStages LDS
@@ -91,12 +83,12 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
 // wave instruction is 16 rows x 64 B; lane l fills row l/4, slot l%4 and so
 // loads the row's logical chunk (l%4) ^ swz(row).
 //
-// e4m3 weights stay e4m3 in LDS (32-byte rows, two 16-byte halves swapped on
-// bit 2 of the row) and are widened exactly to bf16 when a fragment is read.
+// e4m3 k-tiles are 64 wide: a B row is 64 e4m3 bytes in the same swizzled
+// 64-byte layout, and A holds two such 64-byte halves (k 0..31, k 32..63)
+// one after the other.
 constexpr int kStages = 4;
-constexpr int A_STAGE = BM * BK * 2;          // bytes of one A stage (16 KB)
-constexpr int B_STAGE_BF16 = BN * BK * 2;     // 16 KB
-constexpr int B_STAGE_E4M3 = BN * BK;         // 8 KB
+constexpr int A_STAGE = BM * BK * 2;          // bytes of one 64-byte-row A half (16 KB)
+constexpr int B_STAGE = BN * 64;              // 256 rows x 64 B (16 KB)
 constexpr int kOutPitch = 80;                 // bytes per row of a wave's 32 x 32 bf16 output patch
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 1 | (((r >> 2) & 1) << 1); }
@@ -172,16 +164,11 @@ __device__ __forceinline__ void wait_barrier_dyn(int n) {
     }
 }
 
-// 8 e4m3 codes (two dwords) -> bf16x8, exact.
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint2 v) {
-    const uint2 lo = e4m3x4_to_bf16x4(v.x), hi = e4m3x4_to_bf16x4(v.y);
-    const uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    return __builtin_bit_cast(bf16x8, u);
-}
-
 // Wave tile 128 x 64: wave (wm, wn) owns the 32-row blocks wm, wm+2, wm+4,
 // wm+6 (interleaved, so a half-filled tile keeps both M-waves busy) and B
-// rows wn*64 .. wn*64+63.  The MFMA is issued as B x A^T so each lane ends
+// rows wn*64 .. wn*64+63.  wm = wave / 4: the waves of a workgroup are dealt
+// round-robin over the 4 SIMDs of the CU, so on a tile of at most 32 rows
+// (where only wm = 0 has MFMA work) the 4 busy waves have a SIMD each.  The MFMA is issued as B x A^T so each lane ends
 // with 4 consecutive output columns of one row: for acc register r of a
 // 32x32 block, row = lane % 32, column = 8*(r/4) + 4*(lane/32) + r%4.
 //
@@ -193,15 +180,21 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint2 v) {
 template <int EPI, bool FP8, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int NT = NW * 64;                  // threads
-    constexpr int B_STAGE = FP8 ? B_STAGE_E4M3 : B_STAGE_BF16;
+    constexpr int BKT = FP8 ? 64 : BK;           // k per k-tile: 64-byte weight-row pieces
+    constexpr int AM = BKT / BK;                 // 64-byte A halves per k-tile
+    constexpr int STG = FP8 ? 3 : kStages;       // ring stages (3 x 48 KB or 4 x 32 KB)
+    constexpr int A_ST = AM * A_STAGE;           // bytes of one A stage
+    constexpr int WB = FP8 ? 1 : 2;              // weight bytes per element
+    constexpr bool OUT_IN_RING = FP8;            // epilogue patch in the ring slot just used
     constexpr int BW = BN / (NW / 2);            // B rows (wave tile columns) per wave: 64 or 128
     constexpr int NBW = BW / 32;                 // 32-column MFMA blocks per wave: 2 or 4
-    constexpr int LB = (FP8 ? 8 : 16) / NW;      // B DMA instructions per thread per k-tile
+    constexpr int LB = 16 / NW;                  // B DMA instructions per thread per k-tile
     constexpr int GA = 16 / NW;                  // A 16-row groups per wave: 2 or 4
-    __shared__ __attribute__((aligned(1024))) unsigned char sA[kStages][A_STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char sB[kStages][B_STAGE];
+    static_assert(!OUT_IN_RING || NW * 32 * kOutPitch <= A_ST, "output patch fits in an A stage");
+    __shared__ __attribute__((aligned(1024))) unsigned char sA[STG][A_ST];
+    __shared__ __attribute__((aligned(1024))) unsigned char sB[STG][B_STAGE];
     __shared__ int32_t s_mt[kMaxGroupsLds + 1], s_off[kMaxGroupsLds + 1];
-    __shared__ __attribute__((aligned(16))) unsigned char sOut[NW][32 * kOutPitch];
+    __shared__ __attribute__((aligned(16))) unsigned char sOut[OUT_IN_RING ? 1 : NW][OUT_IN_RING ? 16 : 32 * kOutPitch];
     // EPI_COMBINE: the tile's routes and their weights, loaded during the
     // k-loop by direct-to-LDS loads (plain loads in the epilogue would wait
     // for every k-tile of the next tile already in flight)
@@ -209,7 +202,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     __shared__ float s_rw[EPI == EPI_COMBINE ? BM : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave / (NW / 2), wn = wave % (NW / 2);
     const bool uniform = a.mt_off == nullptr;
     int total_mt, tiles_per_group = 0;
     if (uniform) {
@@ -235,14 +228,16 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
 
     const char* Ab = (const char*)a.A;
     const char* Bb = (const char*)a.B;
-    const int nk = a.K / BK;
+    const int nk = a.K / BKT;
+    // ring slot of a running k-tile count
+    auto ring = [](int x) { return (STG & (STG - 1)) == 0 ? (x & (STG - 1)) : (x % STG); };
 
     // DMA plan.  A: wave w fills the 16-row groups w + NW*i (row 16*group +
     // lane/4), i < GA; with 8 waves a group wholly past the expert's last row
     // is not loaded, so a half-filled tile issues half the A traffic and
-    // every wave still has one A group while rows > 128.  bf16 B: wave w
-    // fills rows w*16*LB + 16*b + lane/4 (b < LB).  e4m3 B: wave w fills rows
-    // w*32*LB + 32*b + lane/2, 16-byte half lane%2.
+    // every wave still has one A group while rows > 128; a 64-wide k-tile
+    // loads each group twice (both halves).  B: wave w fills rows
+    // w*16*LB + 16*b + lane/4 (b < LB), 64 bytes per row (32 bf16 or 64 e4m3).
     const int dr = lane >> 2, ds = lane & 3;
 
     // wave-uniform LDS bases of this wave's DMA blocks in ring slot 0
@@ -250,7 +245,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     const uint32_t rq0 = __builtin_amdgcn_readfirstlane(lds_addr(s_rq) + wave * 256);
     const uint32_t rw0 = __builtin_amdgcn_readfirstlane(lds_addr(s_rw) + wave * 256);
     // routes of the epilogue staged in LDS: needs k-tiles 1, 5 and 9 (see the k-loop)
-    const bool route_pf = EPI == EPI_COMBINE && a.K / BK >= 10;
+    const bool route_pf = EPI == EPI_COMBINE && nk >= 10;
     const uint32_t lb0 = __builtin_amdgcn_readfirstlane(lds_addr(sB[0]) + wave * LB * 1024);
 
     // A tile's place in the problem and this thread's DMA sources (byte
@@ -310,16 +305,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
             const int ra = (wave + NW * i) * 16 + dr;
             t.ga[i] = ar[i] * a.lda * 2 + ((ds ^ swz(ra)) * 16);
         }
-        t.gbase = (int64_t)g * a.b_group_stride * (FP8 ? 1 : 2);
+        t.gbase = (int64_t)g * a.b_group_stride * WB;
 #pragma unroll
         for (int b = 0; b < LB; ++b) {
-            if (FP8) {
-                const int rb = wave * 32 * LB + 32 * b + (lane >> 1), hb = lane & 1;
-                t.gb[b] = (uint32_t)brow_of(rb) * (uint32_t)a.k_seg + ((hb ^ ((rb >> 2) & 1)) * 16);
-            } else {
-                const int rb = wave * 16 * LB + 16 * b + dr;
-                t.gb[b] = (uint32_t)brow_of(rb) * (uint32_t)a.k_seg * 2 + ((ds ^ swz(rb)) * 16);
-            }
+            const int rb = wave * 16 * LB + 16 * b + dr;
+            t.gb[b] = (uint32_t)brow_of(rb) * (uint32_t)a.k_seg * WB + ((ds ^ swz(rb)) * 16);
         }
         // K order: the tile starts at k-tile `rot` and wraps.  Tiles of
         // different experts running at the same time then read different
@@ -337,21 +327,23 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     auto issue = [&](const Tile& t, int s, int slot) {
         int kr = s + t.rot;
         if (kr >= nk) kr -= nk;
-        const int k0 = kr * BK;
+        const int k0 = kr * BKT;
         const int seg = k0 / a.k_seg;
         const int64_t bo = (int64_t)seg * a.b_seg_stride + (k0 - seg * a.k_seg);
-        const uint32_t la = la0 + slot * A_STAGE, lb = lb0 + slot * B_STAGE;
+        const uint32_t la = la0 + slot * A_ST, lb = lb0 + slot * B_STAGE;
 #pragma unroll
-        for (int i = 0; i < GA; ++i)
-            if (t.la > i) dma16(Ab + t.ga[i] + (int64_t)k0 * 2, la + i * NW * 1024);
+        for (int h = 0; h < AM; ++h)
 #pragma unroll
-        for (int b = 0; b < LB; ++b) dma16(Bb + t.gbase + t.gb[b] + bo * (FP8 ? 1 : 2), lb + b * 1024);
+            for (int i = 0; i < GA; ++i)
+                if (t.la > i) dma16(Ab + t.ga[i] + (int64_t)(k0 + h * BK) * 2, la + h * A_STAGE + i * NW * 1024);
+#pragma unroll
+        for (int b = 0; b < LB; ++b) dma16(Bb + t.gbase + t.gb[b] + bo * WB, lb + b * 1024);
     };
 
     // The load ring runs across tiles: while a tile's last kStages - 1
     // k-tiles are multiplied, the next tile's first ones are loaded, so the
     // pipeline never drains between tiles.  Ring slot of k-tile s of a tile =
-    // (sbase + s) % kStages, sbase = k-tiles of this workgroup's earlier tiles.
+    // (sbase + s) % STG, sbase = k-tiles of this workgroup's earlier tiles (mod STG).
     // Every wait bounds the number of this thread's DMA instructions issued
     // after the awaited k-tile; other outstanding loads and stores (the
     // next tile's row lookups, the epilogue's stores) only make it stricter.
@@ -360,13 +352,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     Tile cur = make_tile(Lt);
     int sbase = 0;
 #pragma unroll
-    for (int st = 0; st < kStages - 1; ++st) issue(cur, st, st);   // nk >= 4
+    for (int st = 0; st < STG - 1; ++st) issue(cur, st, st);   // nk >= STG - 1 (K >= 128)
 
     const int rA = lane & 31, half = lane >> 5;
     for (; Lt < total; Lt += G) {
         const bool has_next = Lt + G < total;
         const Tile nxt = has_next ? make_tile(Lt + G) : cur;
-        const int cn = has_next ? LB + nxt.la : 0;   // next tile's DMA count per k-tile
+        const int cn = has_next ? LB + AM * nxt.la : 0;   // next tile's DMA count per k-tile
         const int g = cur.g, nt = cur.nt, a_row0 = cur.a_row0, rows = cur.rows;
 
         f32x16 acc[4][NBW];
@@ -388,16 +380,21 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
         auto kloop = [&](auto na_c, auto la_c) {
             constexpr int NA = decltype(na_c)::value;
             constexpr int LA = decltype(la_c)::value;
-            constexpr int LC = LB + LA;   // this tile's DMA count per k-tile
+            constexpr int LC = LB + AM * LA;   // this tile's DMA count per k-tile
             for (int kt = 0; kt < nk; ++kt) {
-                // in flight behind k-tile kt: k-tiles kt + 1 and kt + 2, of this
-                // tile or (at the end) of the next one
-                if (kt + 2 < nk) waitcnt_barrier<2 * LC>();
-                else if (kt + 2 == nk) wait_barrier_dyn(LC + cn);
-                else wait_barrier_dyn(2 * cn);
-                const int s = kt + kStages - 1;
-                if (s < nk) issue(cur, s, (sbase + s) & (kStages - 1));
-                else if (has_next) issue(nxt, s - nk, (sbase + s) & (kStages - 1));
+                // in flight behind k-tile kt: k-tiles kt + 1 .. kt + STG - 2, of
+                // this tile or (at the end) of the next one
+                if (STG == 4) {
+                    if (kt + 2 < nk) waitcnt_barrier<2 * LC>();
+                    else if (kt + 2 == nk) wait_barrier_dyn(LC + cn);
+                    else wait_barrier_dyn(2 * cn);
+                } else {
+                    if (kt + 1 < nk) waitcnt_barrier<LC>();
+                    else wait_barrier_dyn(cn);
+                }
+                const int s = kt + STG - 1;
+                if (s < nk) issue(cur, s, ring(sbase + s));
+                else if (has_next) issue(nxt, s - nk, ring(sbase + s));
                 if (EPI == EPI_COMBINE && route_pf && wave < 4) {
                     // waves 0..3 stage the routes of tile rows 64 wave + lane at
                     // k-tile 1 (every wave has left the previous tile's
@@ -411,20 +408,21 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
                     }
                 }
                 if (NA == 0) continue;
-                const int slot = (sbase + kt) & (kStages - 1);
-                const unsigned char* sa = sA[slot];
+                const int slot = ring(sbase + kt);
                 const unsigned char* sb = sB[slot];
 #pragma unroll
-                for (int ks = 0; ks < BK / 16; ++ks) {
-                    const int c = ks * 2 + half;  // logical 16-byte chunk of this lane
+                for (int ks = 0; ks < BKT / 16; ++ks) {
+                    // this lane's k = 16 ks + 8 half .. + 7: logical 16-byte chunk c
+                    // of the 64-byte A half ks / 2 and of a bf16 B row; in an e4m3
+                    // B row, the 8-byte piece `half` of chunk ks
+                    const int c = (ks & 1) * 2 + half;
+                    const unsigned char* sa = sA[slot] + (ks >> 1) * A_STAGE;
                     bf16x8 bv[NBW], av[NA > 0 ? NA : 1];
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb) {
                         const int r = wn * BW + nb * 32 + rA;
                         if (FP8) {
-                            // piece c (8 bytes) of a 32-byte row; halves swapped on row bit 2
-                            const int pc = ((c >> 1) ^ ((r >> 2) & 1)) * 16 + (c & 1) * 8;
-                            bv[nb] = e4m3x8_to_bf16x8(*(const uint2*)(sb + r * 32 + pc));
+                            bv[nb] = e4m3x8_to_bf16x8(*(const uint2*)(sb + r * 64 + ((ks ^ swz(r)) * 16) + half * 8));
                         } else {
                             bv[nb] = *(const bf16x8*)(sb + r * 64 + ((c ^ swz(r)) * 16));
                         }
@@ -462,7 +460,16 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
         // instruction writes 16 rows x 64 contiguous bytes instead of 16-byte
         // pieces of 32 rows; float32 results are stored directly ----
         const int c4 = 4 * (lane >> 5);
-        unsigned char* so = sOut[wave];
+        unsigned char* so;
+        if (OUT_IN_RING) {
+            // every wave has read its last fragments of the k-tile just
+            // multiplied (its LDS reads are complete before the barrier); its
+            // slot is refilled only after the next tile's first barrier
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            so = sA[ring(sbase + nk - 1)] + wave * 32 * kOutPitch;
+        } else {
+            so = sOut[wave];
+        }
         const int sr = lane >> 2, sq = lane & 3;   // store phase: row (of 16), 16-byte chunk
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -546,7 +553,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
                 }
             }
         }
-        sbase += nk;
+        sbase = ring(sbase + nk);
         cur = nxt;
     }
 }

@@ -32,6 +32,10 @@ SMALL = {
     "relu2_small": ("relu2_distinct_R8", dict(H=256, I=256)),
     "decode_shared_small": ("decode_T8", dict(T=37, H=256, I=128, I_shared=256, C=37)),
     "fp8_small": ("skewed_fp8", dict(T=300, H=256, E=8, I=256, C=96)),
+    # e4m3 weights with K >= 640 in both projections (64-wide k-tiles: the
+    # combine epilogue's routes staged in LDS) over two m-tiles per expert,
+    # the second ragged, and a ragged last n-tile
+    "fp8_k640_two_mtiles": ("skewed_fp8", dict(T=600, H=768, E=4, k=2, I=640, C=600)),
     "k1_e1": ("prefill_T256", dict(T=130, H=128, E=1, k=1, I=128, C=130)),
     "fp32_relu2_renorm": ("tiny_fp32", dict(act=synth.ACT_RELU2, renormalize=1, T=100, C=40)),
     # hidden / intermediate not multiples of the 256-column tile
@@ -357,6 +361,46 @@ def test_forward_small(key):
     _check_meta(cs, meta, r)
     assert n_bad == 0
     assert_close(cs, out, r["out"], "out")
+
+
+@pytest.mark.parametrize("T", [1, 300])   # slot-indexed decode kernels; tiled expert GEMMs
+def test_forward_e4m3_widening_exact(T):
+    """Every finite e4m3 code through the expert GEMMs, bit-exact.  ReLU-square
+    experts with x = e_0 and a gate row 0 of 1.0 give h = e_0, so output
+    column o of the down projection is the e4m3 weight w2[o, 0] times a
+    per-row scale of 1.  With logits +16 / -16 and top-1 the routing weight
+    is exactly 1 (softmax of two logits 32 apart rounds to 1 in float32), so
+    every output value is the widened code itself; e4m3 values are bf16
+    values, so nothing may round.  Expected values: torch's float8_e4m3fn
+    decoding on the CPU (-0.0 as +0.0, see below)."""
+    H, I, E = 256, 128, 2
+    cs = synth.Case("e4m3_codes", T=T, H=H, E=E, k=1, I=I, C=T, act=synth.ACT_RELU2,
+                    w_fmt=synth.FMT_E4M3)
+    _say("e4m3 widening", T)
+    codes = torch.arange(256, dtype=torch.int32)
+    codes[(codes & 0x7F) == 0x7F] = 0                      # the two NaN codes
+    codes = codes.to(torch.uint8)
+    x = torch.zeros((T, H), dtype=torch.bfloat16)
+    x[:, 0] = 1.0
+    lg = torch.full((T, E), -16.0)
+    lg[:, 0] = 16.0
+    w13 = torch.zeros((E, I, H), dtype=torch.uint8)
+    w13[:, 0, 0] = 0x38                                      # e4m3 1.0
+    w2 = torch.zeros((E, H, I), dtype=torch.uint8)
+    w2[:, :, 0] = codes
+    inp = synth.Inputs(cs, x.to(DEV), lg.to(DEV), w13.to(DEV), w2.to(DEV),
+                       torch.ones((E, I), device=DEV), torch.ones((E, H), device=DEV))
+    out, meta, n_bad = _forward_gpu(cs, inp)
+    assert n_bad == 0
+    np.testing.assert_array_equal(np_i32(meta["ids"]), np.zeros((T, 1), np.int32))
+    assert torch.equal(meta["w"].cpu(), torch.ones((T, 1)))
+    want = codes.view(torch.float8_e4m3fn).float()
+    # the code 0x80 (-0.0) reaches the output through a sum of products that
+    # starts from +0, and +0 + (-0) = +0
+    want = torch.where(want == 0, torch.zeros_like(want), want).to(torch.bfloat16)
+    got = out.cpu()
+    bad = (got.view(torch.int16) != want.view(torch.int16).expand(T, H)).nonzero()
+    assert bad.numel() == 0, f"{bad.shape[0]} values differ, first (token, code) {bad[0].tolist()}"
 
 
 @pytest.mark.parametrize("key", FULL)
