@@ -23,6 +23,9 @@
 // at a time, each wavefront on a quarter of K; the four partial sums are
 // added in LDS in wavefront order.
 //
+// K order: a work item starts at K group (13 expert + 7 block) mod its group
+// count and wraps (see Item::rot).
+//
 // Loads: each wavefront owns a private 32 KB LDS ring of stages (4 stages of
 // 32 activation rows and 32 weight rows of 128 bytes) filled by direct
 // global -> LDS loads; it waits only on its own vector-memory counter (no
@@ -167,6 +170,7 @@ struct Item {
     int base, rows, m0;     // expert's first row, its row count, this block's first row
     int mrows;              // rows in this block
     int g0, nK;             // first K group of this wavefront, K groups
+    int rot;                // K group this wavefront starts at (0 .. nK-1), then wraps
     int32_t q;              // combine epilogue: route of this lane's row
     float cw;               // and its weight
     const char* asrc[4];
@@ -227,6 +231,12 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
         const int kq = SPLIT ? (nKall + kDWaves - 1) / kDWaves : nKall;
         it.g0 = SPLIT ? min(nKall, wave * kq) : 0;
         it.nK = min(nKall, it.g0 + kq) - it.g0;
+        // units running at the same time start at different K groups, so the
+        // weight rows (a power-of-two stride apart) are not all read at the
+        // same column offset, which would load a few memory channels only;
+        // the start depends on the expert and the weight block alone, so a
+        // row's summation order never depends on the other tokens
+        it.rot = it.nK > 0 ? (it.group * 13 + it.blk * 7) % it.nK : 0;
         const bool fp8 = FP8 && it.si == 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -280,7 +290,9 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     auto issue = [&](const Item& it, int gk, int slot) {
         const DecodeSeg& s = d.seg[it.si];
         const bool fp8 = FP8 && it.si == 0;
-        const int k0 = (it.g0 + gk) * kDGroupK;
+        int gr = gk + it.rot;
+        if (gr >= it.nK) gr -= it.nK;
+        const int k0 = (it.g0 + gr) * kDGroupK;
         const int seg = k0 / s.k_seg;
         const int64_t kb = (int64_t)seg * s.b_seg_stride + (k0 - seg * s.k_seg);
         const uint32_t st = ring0 + slot * RG::STAGE;
