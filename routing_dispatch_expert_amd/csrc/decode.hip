@@ -47,6 +47,7 @@ namespace {
 constexpr int kDWaves = 4;          // wavefronts per workgroup
 constexpr int kDRing = 32768;       // LDS ring bytes per wavefront
 constexpr int kDGroupK = 64;        // K elements per stage
+constexpr int kDStageRows = 1024;   // kept rows whose routes (and weights) are staged in LDS
 
 // Stage layout: AR activation rows then 32 weight rows, 128 bytes each.
 template <bool SMALLM>
@@ -197,12 +198,29 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // tile table and row ranges of segment 0 when it is routed
     __shared__ int32_t s_mt[kDecodeMaxGroups + 1], s_off[kDecodeMaxGroups + 1];
+    // and, for batches of at most kDStageRows kept rows, each row's route and
+    // (down projection) its combine weight: a work item then finds its
+    // activation rows and weights in LDS instead of through two dependent
+    // global loads made while its ring is empty
+    __shared__ int32_t s_rs[kDStageRows];
+    __shared__ float s_rw[EPI0 == EPI_COMBINE ? kDStageRows : 1];
+    bool staged = false;   // workgroup-uniform
     if (d.seg[0].mt) {
         for (int i = threadIdx.x; i <= d.seg[0].n_groups; i += blockDim.x) {
             s_mt[i] = d.seg[0].mt[i];
             s_off[i] = d.seg[0].offsets[i];
         }
         __syncthreads();
+        const int R = s_off[d.seg[0].n_groups];
+        staged = (d.seg[0].gather || EPI0 == EPI_COMBINE) && R <= kDStageRows;
+        if (staged) {
+            for (int i = threadIdx.x; i < R; i += blockDim.x) {
+                const int32_t q = d.row_src[i];
+                s_rs[i] = q;
+                if (EPI0 == EPI_COMBINE) s_rw[i] = d.route_w[q];
+            }
+            __syncthreads();
+        }
     }
     // work items: 32-row tiles x weight blocks; routed segments own tiles only
     // for experts with rows (tile table), uniform ones ceil(rows / 32) per group
@@ -246,7 +264,10 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
                 const int m = min(r, it.mrows - 1);
                 int64_t arow;
                 if (s.offsets == nullptr) arow = (int64_t)(m0 + m);                            // uniform rows
-                else if (s.gather) arow = (int64_t)(d.row_src[it.base + m0 + m] / d.k_top);      // token of the route
+                else if (s.gather) {                                                             // token of the route
+                    const int rr = it.base + m0 + m;
+                    arow = (int64_t)((staged && it.si == 0 ? s_rs[rr] : d.row_src[rr]) / d.k_top);
+                }
                 else arow = (int64_t)(it.base + m0 + m);
                 it.asrc[i] = (const char*)s.A + (arow * s.lda) * 2 + c * 16;
             }
@@ -283,8 +304,14 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
         setup(it, m0);
         if ((it.si == 0 ? EPI0 : EPI1) == EPI_COMBINE) {
             const int m = min(lane & 31, it.mrows - 1);
-            it.q = d.row_src[it.base + m0 + m];
-            it.cw = d.route_w[it.q];
+            const int rr = it.base + m0 + m;
+            if (staged && it.si == 0) {
+                it.q = s_rs[rr];
+                it.cw = s_rw[rr];
+            } else {
+                it.q = d.row_src[rr];
+                it.cw = d.route_w[it.q];
+            }
         }
     };
     auto issue = [&](const Item& it, int gk, int slot) {

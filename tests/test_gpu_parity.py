@@ -47,6 +47,9 @@ SMALL = {
     # decode-shaped (few rows per expert): slot-indexed expert GEMMs
     "decode_fp8": ("skewed_fp8", dict(T=16, H=256, E=32, k=4, I=256, C=16)),
     "decode_rows_over_32": ("skewed_bf16", dict(T=180, H=256, E=32, k=2, I=128, C=180)),
+    # decode-shaped with more than 1024 kept rows (1280): routes read from
+    # global memory instead of the kernel's LDS copy
+    "decode_rows_over_1024": ("prefill_T256", dict(T=160, H=256, E=128, k=8, I=128, C=160)),
     "decode_shared_T64": ("decode_T32", dict(T=64, H=256, I=128, I_shared=256, C=64)),
     # sigmoid routing with a selection-only bias, normalised and scaled weights
     "sigmoid_relu2_small": ("sigmoid_relu2_R16", dict(H=256, I=256)),
