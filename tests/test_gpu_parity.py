@@ -51,6 +51,9 @@ SMALL = {
     # global memory instead of the kernel's LDS copy
     "decode_rows_over_1024": ("prefill_T256", dict(T=160, H=256, E=128, k=8, I=128, C=160)),
     "decode_shared_T64": ("decode_T32", dict(T=64, H=256, I=128, I_shared=256, C=64)),
+    # the largest expert count (1024): the expert GEMMs' LDS tile tables full
+    "e1024_prefill": ("prefill_T256", dict(T=2048, H=128, E=1024, k=8, I=128, C=2048)),
+    "e1024_decode": ("decode_T8", dict(T=64, H=128, E=1024, k=8, I=128, I_shared=128, C=64)),
     # sigmoid routing with a selection-only bias, normalised and scaled weights
     "sigmoid_relu2_small": ("sigmoid_relu2_R16", dict(H=256, I=256)),
     "sigmoid_prefill_small": ("sigmoid_T2048", dict(T=300, H=256, E=16, k=4, I=256, C=300)),
