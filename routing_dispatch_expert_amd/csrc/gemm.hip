@@ -273,9 +273,18 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
             const int loc = (int)(Lt - (int64_t)s_mt[t.g] * ntl);
             t.nt = loc / cnt;
             ml = loc - t.nt * cnt;
-            const int e0 = s_off[t.g], e1 = s_off[t.g + 1];
-            t.a_row0 = e0 + ml * BM;
-            t.rows = min(BM, e1 - t.a_row0);
+            // an expert's n rows are spread evenly over its cnt = ceil(n / BM)
+            // m-tiles, so that a remainder of a few rows does not get a tile
+            // of its own that streams the whole weight tile for almost no
+            // MFMA work.  per = ceil(n / cnt) <= BM, rounded up to whole
+            // 32-row MFMA blocks while the last tile keeps at least one row;
+            // (cnt - 1) per < n <= cnt per either way
+            const int e0 = s_off[t.g], e1 = s_off[t.g + 1], n = e1 - e0;
+            int per = (n + cnt - 1) / cnt;
+            const int p32 = (per + 31) & ~31;
+            if (p32 <= BM && (cnt - 1) * p32 < n) per = p32;
+            t.a_row0 = e0 + ml * per;
+            t.rows = min(per, e1 - t.a_row0);
         }
         const int g = t.g, nt = t.nt, rows = t.rows;
         // B row r of the tile: for SwiGLU each wave's BW rows are BW/2 gate
