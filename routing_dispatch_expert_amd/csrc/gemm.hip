@@ -71,6 +71,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // stages filled by direct global -> LDS loads (global_load_lds_dwordx4: lane l
 // of a wave writes the 16 bytes it loads to LDS base + 16*l).  kStages - 1
 // k-tiles are in flight while one is multiplied; one barrier per k-tile.
+// (e4m3 weights: 64-wide k-tiles in a ring of 3 stages, 2 in flight.)
 //
 // Each tile walks K starting at a rotated k-tile (see `rot` below).
 //
