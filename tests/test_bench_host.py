@@ -49,3 +49,25 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert p.returncode == 2
     assert "one GPU" in p.stderr
+
+
+def test_dispatch_bytes_count_the_row_copy():
+    # moe_dispatch with x_disp: ids read, counts / offsets / route_dst /
+    # row_src written, every token row read once, one copy per kept route
+    cs = synth.case("prefill_T2048")
+    route, disp = bench.dispatch_bytes(cs, R=16384)
+    Q = 2048 * 8
+    assert route == 2048 * 128 * 4 + Q * 8
+    assert disp == Q * 4 + 128 * 4 + 129 * 4 + Q * 4 + 16384 * 4 + 2048 * 2048 * 2 + 16384 * 2048 * 2
+    assert round(disp / 1e6, 1) == 75.7
+
+
+def test_forward_scatter_bytes_are_metadata_only_for_bf16():
+    # bf16 layers place routes only (the expert GEMM reads x in place);
+    # float32 layers copy the rows
+    bf = bench.stage_bytes_flops(synth.case("prefill_T2048"), 16384, 128, 2, 2)
+    Q = 2048 * 8
+    assert bf["scatter"][0] == Q * 16 + Q * 4
+    f32 = synth.case("tiny_fp32")
+    bf32 = bench.stage_bytes_flops(f32, 128, 16, 4, 4)
+    assert bf32["scatter"][0] == 64 * 256 * 4 + 128 * 256 * 4 + 128 * 16 + 128 * 4
