@@ -364,12 +364,17 @@ DecodeSeg shared_seg2(const moe_problem& p, const void* h_sh, const void* w2_sh,
 
 // max_rows: a bound on the rows of any group known to hold (-1: none); 8 or
 // fewer selects the 8-row activation staging.
+// fused: the launch routes and dispatches the batch itself (gate/up only).
 hipError_t run_decode(const DecodeSeg* a, const DecodeSeg* b, const int32_t* row_src, int k,
                       const float* route_w, int w_dtype, int64_t route_count, int max_rows,
-                      hipStream_t s) {
+                      hipStream_t s, const DecodeFused* fused = nullptr) {
     DecodeArgs d = {};
     d.seg[0] = a ? *a : *b;
     d.n_seg = 1;
+    if (fused) {
+        d.use_fused = 1;
+        d.fused = *fused;
+    }
     if (a && b) {
         d.seg[1] = *b;
         d.n_seg = 2;
@@ -578,7 +583,14 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
         if (e == hipSuccess && m.w && m.w != w_in) e = launch_copy_u32(m.w, w_in, Q, s);
     }
     if (e != hipSuccess) return MOE_ERR_HIP;
-    if (in_place && P.T <= kSmallMaxT && P.E <= kSmallMaxE) {
+    // batches of a few tokens with softmax routing: the gate/up decode launch
+    // routes and dispatches them itself, one launch fewer
+    const bool fused = dec && !pre && P.T > 0 && P.T <= kFuseMaxT && P.E <= kFuseMaxE &&
+                       P.score_func == MOE_SOFTMAX && P.w_dtype == MOE_BF16;
+    if (fused) {
+        for (int st = MOE_STAGE_ROUTE; e == hipSuccess && st <= MOE_STAGE_SCATTER; ++st) e = mark(m, st, s);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    } else if (in_place && P.T <= kSmallMaxT && P.E <= kSmallMaxE) {
         // small batch: routing and the whole dispatch in one workgroup
         e = launch_small_dispatch(pre ? nullptr : logits, score_bias, pre ? ids_in : nullptr, P.T,
                                   P.k, P.E, P.C, tile_bm, P.score_func, P.renormalize,
@@ -615,7 +627,28 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
         const DecodeSeg sh1 = P.n_shared ? shared_seg1(P, x, w13_sh, h_sh) : DecodeSeg{};
         // rows per group <= T: the dispatch keeps at most one route of a token per
         // expert (a repeated expert is a malformed route), shared groups hold T
-        e = run_decode(&r1, P.n_shared ? &sh1 : nullptr, row_src, P.k, w, P.w_dtype, (int64_t)P.T * P.k, P.T, s);
+        DecodeFused fz = {};
+        if (fused) {
+            fz.logits = logits;
+            fz.T = P.T;
+            fz.k = P.k;
+            fz.E = P.E;
+            while ((1 << fz.ebits) < P.E) ++fz.ebits;
+            fz.C = P.C;
+            fz.renorm = P.renormalize;
+            fz.scale = route_scale_of(P);
+            fz.ids = ids_out;
+            fz.w = w_out;
+            fz.counts = counts;
+            fz.offsets = offsets;
+            fz.mt = mt;
+            fz.row_src = row_src;
+            fz.route_dst = route_dst;
+            fz.ctrl = at<int32_t>(ws, L.ctrl);
+            fz.r_max = r_max_of(P);
+        }
+        e = run_decode(&r1, P.n_shared ? &sh1 : nullptr, row_src, P.k, w, P.w_dtype, (int64_t)P.T * P.k, P.T, s,
+                       fused ? &fz : nullptr);
         if (e == hipSuccess) e = mark(m, MOE_STAGE_GEMM1, s);
         if (e != hipSuccess) return MOE_ERR_HIP;
         const DecodeSeg r2 = routed_seg2(P, h, offsets, mt, w2, s2, EPI_COMBINE, ybuf);

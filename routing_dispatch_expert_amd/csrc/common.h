@@ -145,12 +145,34 @@ struct DecodeSeg {
     int n_groups;
     int blocks;
 };
+// Routing and dispatch done inside the gate/up launch for batches of at most
+// kFuseMaxT tokens over at most kFuseMaxE experts with softmax routing: every
+// workgroup computes the routes, ranks, offsets and tile table into LDS and
+// workgroup 0 writes the metadata that later launches and the caller read.
+constexpr int kFuseMaxT = 8;
+constexpr int kFuseMaxE = 256;
+struct DecodeFused {
+    const float* logits;    // [T, E]
+    int T, k, E, ebits, C, renorm;
+    float scale;
+    int32_t* ids;           // [T, k]
+    float* w;               // [T, k]
+    int32_t* counts;        // [E]
+    int32_t* offsets;       // [E + 1]
+    int32_t* mt;            // [E + 1], 32-row tiles
+    int32_t* row_src;       // [r_max]
+    int32_t* route_dst;     // [T, k]
+    int32_t* ctrl;
+    int64_t r_max;
+};
 struct DecodeArgs {
     DecodeSeg seg[2];
     int n_seg;
     const int32_t* row_src;
     int k_top;
     const float* route_w;
+    int use_fused;          // segment 0's routes come from `fused`
+    DecodeFused fused;
 };
 // small_m: no group has more than 8 rows (the 8-row staging of the decode ring)
 hipError_t launch_decode_gemm(const DecodeArgs& d, int w_dtype, int split, int small_m, int grid,

@@ -39,7 +39,7 @@
 // operands leaves the product unchanged), so each lane's bytes for a group
 // are one 64-byte run.  16-byte chunk c of row r sits at chunk slot
 // c ^ ((r ^ r >> 3) & 7): the fragment reads are free of bank conflicts.
-#include "common.h"
+#include "route_wave.h"
 
 namespace rde {
 namespace {
@@ -163,6 +163,166 @@ __device__ __forceinline__ void epilogue(const DecodeSeg& s, int group, int blk,
     }
 }
 
+// Inclusive prefix sum over a wavefront (DPP row shifts, then the lower rows'
+// totals) and an exclusive one over a 256-thread workgroup.
+__device__ __forceinline__ int32_t wave_incl_scan_d(int32_t x, int lane) {
+    x += (int32_t)__builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += (int32_t)__builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += (int32_t)__builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += (int32_t)__builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    const int32_t r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+                  r2 = __builtin_amdgcn_readlane(x, 47);
+    if (lane >= 16) x += r0;
+    if (lane >= 32) x += r1;
+    if (lane >= 48) x += r2;
+    return x;
+}
+__device__ int32_t block_excl_scan_256(int32_t v, int32_t* s_w, int32_t& tot) {
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    const int32_t x = wave_incl_scan_d(v, lane);
+    if (lane == kWave - 1) s_w[wv] = x;
+    __syncthreads();
+    int32_t before = 0;
+    for (int w = 0; w < kDWaves; ++w) {
+        if (w < wv) before += s_w[w];
+    }
+    tot = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    __syncthreads();   // s_w is reused by the next scan
+    return before + x - v;
+}
+
+// Routing and count-first dispatch of a batch of at most kFuseMaxT tokens
+// (softmax, at most kFuseMaxE experts), done by every workgroup of a gate/up
+// launch with the same result: routes by the wave routing of route_wave.h
+// (wave w routes tokens w and w + 4), stable ranks of the T*k <= 256 routes
+// (wave w ranks routes 64 w .. 64 w + 63 by ballots over the expert bits, as
+// the count kernel does), per-expert totals, exclusive scans of min(count, C)
+// and of the 32-row tile counts, then each kept route's row.  The offsets,
+// tile table and each row's route land in the kernel's LDS tables; workgroup 0
+// also writes ids, weights, counts, offsets, the tile table, row_src (rows
+// past the kept ones -1) and route_dst.  `scratch` (LDS, 4 E + T k ints) is
+// free again on return.
+__device__ void fused_dispatch(const DecodeFused& f, int32_t* scratch, int32_t* s_mt, int32_t* s_off,
+                               int32_t* s_rs, int32_t* s_w) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const bool writer = blockIdx.x == 0;
+    const int T = f.T, k = f.k, E = f.E, Q = T * k;
+    int32_t* hist = scratch;            // [kDWaves][E]
+    int32_t* sid = scratch + kDWaves * E;   // [Q]
+    {
+        float v[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {   // both rows first: one memory latency
+            const int t = wv + kDWaves * i;
+            if (t < T) load_logits<4>(f.logits + (int64_t)t * E, E, lane, v[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = wv + kDWaves * i;
+            if (t >= T) break;   // wave-uniform
+            int id;
+            float wt;
+            route_row<4, false>(v[i], nullptr, E, k, f.renorm, f.scale, lane, id, wt);
+            if (lane < k) {
+                sid[t * k + lane] = id;
+                if (writer) {
+                    f.ids[t * k + lane] = id;
+                    f.w[t * k + lane] = wt;
+                }
+            }
+        }
+    }
+    for (int i = tid; i < kDWaves * E; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+
+    // ---- stable ranks within each wave's 64 routes ----
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int q = wv * kWave + lane;
+    const bool inq = q < Q;
+    int e = inq ? sid[q] : -1;
+    const bool inrange = inq && e >= 0 && e < E;
+    uint64_t peers = __ballot(inrange);
+    for (int b = 0; b < f.ebits; ++b) {
+        const bool bit = inrange && ((e >> b) & 1);
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    bool dup = false;
+    if (inrange) {
+        const int t = q / k, j = q - t * k;
+        const int first = lane - j;
+        dup = (peers & lt & ~((first > 0) ? (~0ull >> (64 - first)) : 0ull)) != 0;
+        for (int jj = 0; !dup && jj < -first; ++jj) dup = sid[t * k + jj] == e;
+    }
+    int n_bad = 0;
+    if (inq && (!inrange || dup)) {
+        e = -2;
+        n_bad = 1;
+    }
+    peers &= ~__ballot(dup);
+    int32_t* wh = hist + wv * E;
+    int rank = 0;
+    if (e >= 0) {
+        const int before = __popcll(peers & lt);
+        rank = wh[e] + before;          // every lane reads before any lane writes
+        if (before == 0) wh[e] += __popcll(peers);
+    }
+    const int wave_bad = wave_sum_i32(n_bad);
+    if (writer && wave_bad && lane == 0) atomicAdd(&f.ctrl[CTRL_BAD_ROUTES], wave_bad);
+    __syncthreads();
+
+    // ---- per-expert totals and wave bases, then the scans (one expert per thread) ----
+    int32_t kept = 0, tiles = 0;
+    if (tid < E) {
+        int32_t run = 0;
+        for (int w = 0; w < kDWaves; ++w) {
+            const int32_t c = hist[w * E + tid];
+            hist[w * E + tid] = run;
+            run += c;
+        }
+        if (writer) f.counts[tid] = run;
+        kept = run < f.C ? run : f.C;
+        tiles = (kept + kDecodeBM - 1) / kDecodeBM;
+    }
+    int32_t tot_k, tot_t;
+    const int32_t off_e = block_excl_scan_256(kept, s_w, tot_k);
+    const int32_t mt_e = block_excl_scan_256(tiles, s_w, tot_t);
+    if (tid < E) {
+        s_off[tid] = off_e;
+        s_mt[tid] = mt_e;
+        if (writer) {
+            f.offsets[tid] = off_e;
+            f.mt[tid] = mt_e;
+        }
+    }
+    if (tid == 0) {
+        s_off[E] = tot_k;
+        s_mt[E] = tot_t;
+        if (writer) {
+            f.offsets[E] = tot_k;
+            f.mt[E] = tot_t;
+        }
+    }
+    __syncthreads();
+
+    // ---- place every route ----
+    if (inq) {
+        int32_t row = -2;
+        if (e >= 0) {
+            const int32_t r = hist[wv * E + e] + rank;
+            row = r < f.C ? s_off[e] + r : -1;
+            if (row >= 0) {
+                s_rs[row] = q;
+                if (writer) f.row_src[row] = q;
+            }
+        }
+        if (writer) f.route_dst[q] = row;
+    }
+    if (writer)
+        for (int64_t r = tot_k + tid; r < f.r_max; r += blockDim.x) f.row_src[r] = -1;
+    __syncthreads();
+}
+
 // One work item: a unit (32 weight rows of one expert) times a block of up to
 // 32 of the expert's activation rows, over this wavefront's K range.
 struct Item {
@@ -188,7 +348,7 @@ struct Item {
 // them over every CU.  Work items exist only for experts
 // with rows (the dispatch's 32-row tile table, kept in LDS with the experts'
 // row ranges).
-template <int EPI0, int EPI1, bool FP8, bool SPLIT, bool SMALLM>
+template <int EPI0, int EPI1, bool FP8, bool SPLIT, bool SMALLM, bool FUSED>
 __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs d) {
     using RG = DRing<SMALLM>;
     __shared__ __attribute__((aligned(1024))) unsigned char rings[kDWaves][kDRing];
@@ -205,7 +365,13 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     __shared__ int32_t s_rs[kDStageRows];
     __shared__ float s_rw[EPI0 == EPI_COMBINE ? kDStageRows : 1];
     bool staged = false;   // workgroup-uniform
-    if (d.seg[0].mt) {
+    if (FUSED) {
+        // this launch routes and dispatches the batch itself (the ring space is
+        // free until the first work item)
+        __shared__ int32_t s_w4[kDWaves];
+        fused_dispatch(d.fused, (int32_t*)&rings[0][0], s_mt, s_off, s_rs, s_w4);
+        staged = true;   // kept rows <= T k <= kFuseMaxT * 32 <= kDStageRows
+    } else if (d.seg[0].mt) {
         for (int i = threadIdx.x; i <= d.seg[0].n_groups; i += blockDim.x) {
             s_mt[i] = d.seg[0].mt[i];
             s_off[i] = d.seg[0].offsets[i];
@@ -413,11 +579,29 @@ hipError_t launch_decode_gemm(const DecodeArgs& d, int w_dtype, int split, int s
     const int e0 = d.seg[0].epi;
     const int e1 = d.n_seg > 1 ? d.seg[1].epi : ((e0 == EPI_SWIGLU || e0 == EPI_RELU2) ? EPI_SWIGLU : EPI_F32);
     dim3 g(grid), b(kDWaves * 64);
-#define RDE_DEC4(A, B, SM)                                                                              \
-    if (fp8 && split) hipLaunchKernelGGL((decode_gemm_kernel<A, B, true, true, SM>), g, b, 0, st, d);   \
-    else if (fp8) hipLaunchKernelGGL((decode_gemm_kernel<A, B, true, false, SM>), g, b, 0, st, d);      \
-    else if (split) hipLaunchKernelGGL((decode_gemm_kernel<A, B, false, true, SM>), g, b, 0, st, d);    \
-    else hipLaunchKernelGGL((decode_gemm_kernel<A, B, false, false, SM>), g, b, 0, st, d);
+    if (d.use_fused) {
+        // routing inside the launch: bf16 gate/up projections only
+#define RDE_DECF(A, SM)                                                                                           \
+    if (split) hipLaunchKernelGGL((decode_gemm_kernel<A, EPI_SWIGLU, false, true, SM, true>), g, b, 0, st, d);    \
+    else hipLaunchKernelGGL((decode_gemm_kernel<A, EPI_SWIGLU, false, false, SM, true>), g, b, 0, st, d);
+        if (fp8 || e1 != EPI_SWIGLU) return hipErrorInvalidValue;
+        if (e0 == EPI_SWIGLU) {
+            if (small_m) { RDE_DECF(EPI_SWIGLU, true) }
+            else { RDE_DECF(EPI_SWIGLU, false) }
+        } else if (e0 == EPI_RELU2) {
+            if (small_m) { RDE_DECF(EPI_RELU2, true) }
+            else { RDE_DECF(EPI_RELU2, false) }
+        } else {
+            return hipErrorInvalidValue;
+        }
+#undef RDE_DECF
+        return hipGetLastError();
+    }
+#define RDE_DEC4(A, B, SM)                                                                                     \
+    if (fp8 && split) hipLaunchKernelGGL((decode_gemm_kernel<A, B, true, true, SM, false>), g, b, 0, st, d);   \
+    else if (fp8) hipLaunchKernelGGL((decode_gemm_kernel<A, B, true, false, SM, false>), g, b, 0, st, d);      \
+    else if (split) hipLaunchKernelGGL((decode_gemm_kernel<A, B, false, true, SM, false>), g, b, 0, st, d);    \
+    else hipLaunchKernelGGL((decode_gemm_kernel<A, B, false, false, SM, false>), g, b, 0, st, d);
 #define RDE_DEC(A, B)                      \
     if (e0 == A && e1 == B) {              \
         if (small_m) { RDE_DEC4(A, B, true) } \
