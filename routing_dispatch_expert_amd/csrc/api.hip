@@ -585,8 +585,8 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
     if (e != hipSuccess) return MOE_ERR_HIP;
     // batches of a few tokens with softmax routing: the gate/up decode launch
     // routes and dispatches them itself, one launch fewer
-    const bool fused = dec && !pre && P.T > 0 && P.T <= kFuseMaxT && P.E <= kFuseMaxE &&
-                       P.score_func == MOE_SOFTMAX && P.w_dtype == MOE_BF16;
+    const bool fused = dec && !pre && P.T > 0 && P.T <= kFuseMaxT && Q <= kFuseMaxQ &&
+                       P.E <= kFuseMaxE && P.score_func == MOE_SOFTMAX && P.w_dtype == MOE_BF16;
     if (fused) {
         for (int st = MOE_STAGE_ROUTE; e == hipSuccess && st <= MOE_STAGE_SCATTER; ++st) e = mark(m, st, s);
         if (e != hipSuccess) return MOE_ERR_HIP;

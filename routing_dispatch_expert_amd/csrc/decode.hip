@@ -194,7 +194,7 @@ __device__ int32_t block_excl_scan_256(int32_t v, int32_t* s_w, int32_t& tot) {
 // Routing and count-first dispatch of a batch of at most kFuseMaxT tokens
 // (softmax, at most kFuseMaxE experts), done by every workgroup of a gate/up
 // launch with the same result: routes by the wave routing of route_wave.h
-// (wave w routes tokens w and w + 4), stable ranks of the T*k <= 256 routes
+// (wave w routes tokens w, w + 4, ...), stable ranks of the T*k <= 256 routes
 // (wave w ranks routes 64 w .. 64 w + 63 by ballots over the expert bits, as
 // the count kernel does), per-expert totals, exclusive scans of min(count, C)
 // and of the 32-row tile counts, then each kept route's row.  The offsets,
@@ -202,6 +202,11 @@ __device__ int32_t block_excl_scan_256(int32_t v, int32_t* s_w, int32_t& tot) {
 // also writes ids, weights, counts, offsets, the tile table, row_src (rows
 // past the kept ones -1) and route_dst.  `scratch` (LDS, 4 E + T k ints) is
 // free again on return.
+static_assert(kFuseMaxQ == kDWaves * kWave, "one 64-route rank step per wavefront");
+static_assert(kFuseMaxQ <= kDStageRows && kFuseMaxE <= 4 * kWave && kFuseMaxE <= kDecodeMaxGroups,
+              "fused routes staged in LDS; wave routing with 4 experts per lane");
+static_assert(sizeof(int32_t) * (kDWaves * kFuseMaxE + kFuseMaxQ) <= (size_t)kDWaves * kDRing,
+              "fused dispatch scratch fits in the ring space");
 __device__ void fused_dispatch(const DecodeFused& f, int32_t* scratch, int32_t* s_mt, int32_t* s_off,
                                int32_t* s_rs, int32_t* s_w) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
@@ -210,14 +215,15 @@ __device__ void fused_dispatch(const DecodeFused& f, int32_t* scratch, int32_t* 
     int32_t* hist = scratch;            // [kDWaves][E]
     int32_t* sid = scratch + kDWaves * E;   // [Q]
     {
-        float v[2][4];
+        constexpr int TPW = kFuseMaxT / kDWaves;   // tokens per wavefront
+        float v[TPW][4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {   // both rows first: one memory latency
+        for (int i = 0; i < TPW; ++i) {   // all rows first: one memory latency
             const int t = wv + kDWaves * i;
             if (t < T) load_logits<4>(f.logits + (int64_t)t * E, E, lane, v[i]);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < TPW; ++i) {
             const int t = wv + kDWaves * i;
             if (t >= T) break;   // wave-uniform
             int id;
@@ -370,7 +376,7 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
         // free until the first work item)
         __shared__ int32_t s_w4[kDWaves];
         fused_dispatch(d.fused, (int32_t*)&rings[0][0], s_mt, s_off, s_rs, s_w4);
-        staged = true;   // kept rows <= T k <= kFuseMaxT * 32 <= kDStageRows
+        staged = true;   // kept rows <= T k <= kFuseMaxQ <= kDStageRows
     } else if (d.seg[0].mt) {
         for (int i = threadIdx.x; i <= d.seg[0].n_groups; i += blockDim.x) {
             s_mt[i] = d.seg[0].mt[i];

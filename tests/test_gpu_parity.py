@@ -51,6 +51,8 @@ SMALL = {
     # global memory instead of the kernel's LDS copy
     "decode_rows_over_1024": ("prefill_T256", dict(T=160, H=256, E=128, k=8, I=128, C=160)),
     "decode_shared_T64": ("decode_T32", dict(T=64, H=256, I=128, I_shared=256, C=64)),
+    # routing and dispatch inside the gate/up decode launch, with capacity drops
+    "decode_fused_capacity": ("decode_T8", dict(T=8, H=256, E=16, k=8, I=128, I_shared=128, C=2)),
     # the largest expert count (1024): the expert GEMMs' LDS tile tables full
     "e1024_prefill": ("prefill_T256", dict(T=2048, H=128, E=1024, k=8, I=128, C=2048)),
     "e1024_decode": ("decode_T8", dict(T=64, H=128, E=1024, k=8, I=128, I_shared=128, C=64)),
