@@ -604,12 +604,16 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
                              route_scale_of(P), ids_out, w_out, s);
         if (e == hipSuccess) e = mark(m, MOE_STAGE_ROUTE, s);
         if (e != hipSuccess) return MOE_ERR_HIP;
+        // routes that fit one count block are placed by that block when no
+        // rows are copied: no separate scatter launch
+        const bool place = in_place && count_blocks(Q) <= 1;
         e = launch_count_rank(ids, P.T, P.k, P.E, P.C, tile_bm, at<int32_t>(ws, L.rexp),
                               at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), counts, offsets, mt,
-                              at<int32_t>(ws, L.ctrl), s);
+                              at<int32_t>(ws, L.ctrl), s, place ? route_dst : nullptr, row_src,
+                              r_max_of(P));
         if (e == hipSuccess) e = mark(m, MOE_STAGE_COUNT, s);
         if (e != hipSuccess) return MOE_ERR_HIP;
-        if (P.T > 0)
+        if (P.T > 0 && !place)
             e = launch_scatter(x, P.T, P.H, P.k, P.E, P.C, act_bytes(P), r_max_of(P), at<int32_t>(ws, L.rexp),
                                at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), offsets, route_dst,
                                row_src, in_place ? nullptr : x_disp, s);

@@ -61,10 +61,14 @@ hipError_t launch_route(const float* logits, const float* bias, int T, int E, in
 // ids -> rexp (validated expert or -2), lrank (rank inside its block),
 // partial (per-block counts, turned into per-block bases by the last block),
 // counts, offsets and the m-tile table of the grouped GEMM (tile rows bm).
+// With route_dst given and at most kCountBlock routes (one block), the kernel
+// also places the routes (route_dst, row_src with -1 from the kept rows up to
+// r_max), so no metadata scatter is needed.
 hipError_t launch_count_rank(const int32_t* ids, int T, int k, int E, int C, int bm,
                              int32_t* rexp, int32_t* lrank, int32_t* partial,
                              int32_t* counts, int32_t* offsets, int32_t* mt_off,
-                             int32_t* ctrl, hipStream_t s);
+                             int32_t* ctrl, hipStream_t s, int32_t* route_dst = nullptr,
+                             int32_t* row_src = nullptr, int64_t r_max = 0);
 
 // route_dst, row_src and the x -> x_disp row copies.
 hipError_t launch_scatter(const void* x, int T, int H, int k, int E, int C, int elem_bytes,

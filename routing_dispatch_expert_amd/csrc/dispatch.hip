@@ -123,7 +123,8 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
     const int32_t* __restrict__ ids, int64_t Q, int k, int E, int ebits, int C, int bm,
     int32_t* __restrict__ rexp, int32_t* __restrict__ lrank, int32_t* __restrict__ partial,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ mt_off,
-    int32_t* __restrict__ ctrl) {
+    int32_t* __restrict__ ctrl, int32_t* __restrict__ route_dst, int32_t* __restrict__ row_src,
+    int64_t r_max) {
     extern __shared__ int32_t lds[];  // [kCountWaves][E] during counting; [2][E] in the scan
     __shared__ int s_last;
     __shared__ int32_t s_tot[2];
@@ -212,7 +213,8 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
 #pragma unroll
     for (int it = 0; it < kCountPerLane; ++it) {
         const int64_t q = q0 + it * kWave + lane;
-        if (q < Q) lrank[q] = ex[it] >= 0 ? hist[ex[it]] + rank_w[it] : -1;
+        rank_w[it] = ex[it] >= 0 ? hist[ex[it]] + rank_w[it] : -1;   // rank in the block
+        if (q < Q) lrank[q] = rank_w[it];
     }
 
     int32_t* kept = lds;
@@ -240,6 +242,23 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
             tiles[e] = (kp + bm - 1) / bm;
         }
         finish();
+        if (route_dst != nullptr) {
+            // the only block: its ranks are final, so it places the routes
+            // (kept[] holds the offsets after the scan)
+#pragma unroll
+            for (int it = 0; it < kCountPerLane; ++it) {
+                const int64_t q = q0 + it * kWave + lane;
+                if (q >= Q) continue;
+                const int e = ex[it];
+                int32_t row = -2;
+                if (e >= 0) {
+                    row = rank_w[it] < C ? kept[e] + rank_w[it] : -1;
+                    if (row >= 0) row_src[row] = (int32_t)q;
+                }
+                route_dst[q] = row;
+            }
+            for (int64_t r = s_tot[0] + tid; r < r_max; r += blockDim.x) row_src[r] = -1;
+        }
         return;
     }
 
@@ -579,14 +598,17 @@ hipError_t launch_small_dispatch(const float* logits, const float* bias, const i
 
 hipError_t launch_count_rank(const int32_t* ids, int T, int k, int E, int C, int bm, int32_t* rexp,
                              int32_t* lrank, int32_t* partial, int32_t* counts, int32_t* offsets,
-                             int32_t* mt_off, int32_t* ctrl, hipStream_t s) {
+                             int32_t* mt_off, int32_t* ctrl, hipStream_t s, int32_t* route_dst,
+                             int32_t* row_src, int64_t r_max) {
     const int64_t Q = (int64_t)T * k;
     const int nb = count_blocks(Q) > 0 ? count_blocks(Q) : 1;
     int ebits = 1;
     while ((1 << ebits) < E) ++ebits;
     const size_t lds = sizeof(int32_t) * (size_t)kCountWaves * E;
+    if (route_dst != nullptr && nb != 1) return hipErrorInvalidValue;   // placement needs the one block
     hipLaunchKernelGGL(count_rank_kernel, dim3(nb), dim3(kWave * kCountWaves), lds, s, ids, Q, k, E,
-                       ebits, C, bm, rexp, lrank, partial, counts, offsets, mt_off, ctrl);
+                       ebits, C, bm, rexp, lrank, partial, counts, offsets, mt_off, ctrl, route_dst,
+                       row_src, r_max);
     return hipGetLastError();
 }
 

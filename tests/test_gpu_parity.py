@@ -37,6 +37,8 @@ SMALL = {
     # the second ragged, and a ragged last n-tile
     "fp8_k640_two_mtiles": ("skewed_fp8", dict(T=600, H=768, E=4, k=2, I=640, C=600)),
     "k1_e1": ("prefill_T256", dict(T=130, H=128, E=1, k=1, I=128, C=130)),
+    # routes of one count block placed by that block, with capacity drops
+    "one_block_capacity": ("prefill_T256", dict(T=200, H=256, E=8, k=4, I=128, C=50)),
     "fp32_relu2_renorm": ("tiny_fp32", dict(act=synth.ACT_RELU2, renormalize=1, T=100, C=40)),
     # hidden / intermediate not multiples of the 256-column tile
     "ragged_n_relu2": ("relu2_distinct_R8", dict(H=384, I=384)),
