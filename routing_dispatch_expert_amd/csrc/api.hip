@@ -583,10 +583,10 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
         if (e == hipSuccess && m.w && m.w != w_in) e = launch_copy_u32(m.w, w_in, Q, s);
     }
     if (e != hipSuccess) return MOE_ERR_HIP;
-    // batches of a few tokens with softmax routing: the gate/up decode launch
+    // batches of a few tokens with internal routing: the gate/up decode launch
     // routes and dispatches them itself, one launch fewer
     const bool fused = dec && !pre && P.T > 0 && P.T <= kFuseMaxT && Q <= kFuseMaxQ &&
-                       P.E <= kFuseMaxE && P.score_func == MOE_SOFTMAX && P.w_dtype == MOE_BF16;
+                       P.E <= kFuseMaxE && P.w_dtype == MOE_BF16;
     if (fused) {
         for (int st = MOE_STAGE_ROUTE; e == hipSuccess && st <= MOE_STAGE_SCATTER; ++st) e = mark(m, st, s);
         if (e != hipSuccess) return MOE_ERR_HIP;
@@ -634,6 +634,8 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
         DecodeFused fz = {};
         if (fused) {
             fz.logits = logits;
+            fz.bias = score_bias;
+            fz.sigmoid = P.score_func == MOE_SIGMOID;
             fz.T = P.T;
             fz.k = P.k;
             fz.E = P.E;

@@ -192,7 +192,7 @@ __device__ int32_t block_excl_scan_256(int32_t v, int32_t* s_w, int32_t& tot) {
 }
 
 // Routing and count-first dispatch of a batch of at most kFuseMaxT tokens
-// (softmax, at most kFuseMaxE experts), done by every workgroup of a gate/up
+// (softmax or sigmoid, at most kFuseMaxE experts), done by every workgroup of a gate/up
 // launch with the same result: routes by the wave routing of route_wave.h
 // (wave w routes tokens w, w + 4, ...), stable ranks of the T*k <= 256 routes
 // (wave w ranks routes 64 w .. 64 w + 63 by ballots over the expert bits, as
@@ -228,7 +228,8 @@ __device__ void fused_dispatch(const DecodeFused& f, int32_t* scratch, int32_t* 
             if (t >= T) break;   // wave-uniform
             int id;
             float wt;
-            route_row<4, false>(v[i], nullptr, E, k, f.renorm, f.scale, lane, id, wt);
+            if (f.sigmoid) route_row<4, true>(v[i], f.bias, E, k, f.renorm, f.scale, lane, id, wt);
+            else route_row<4, false>(v[i], nullptr, E, k, f.renorm, f.scale, lane, id, wt);
             if (lane < k) {
                 sid[t * k + lane] = id;
                 if (writer) {

@@ -61,6 +61,8 @@ SMALL = {
     # sigmoid routing with a selection-only bias, normalised and scaled weights
     "sigmoid_relu2_small": ("sigmoid_relu2_R16", dict(H=256, I=256)),
     "sigmoid_prefill_small": ("sigmoid_T2048", dict(T=300, H=256, E=16, k=4, I=256, C=300)),
+    # sigmoid routing inside the gate/up decode launch (8 tokens, 240 experts)
+    "sigmoid_decode_fused": ("sigmoid_relu2_R16", dict(T=8, H=256, I=256, C=8)),
 }
 # Full-size workloads.
 FULL = ["tiny_fp32", "prefill_T256", "prefill_T2048", "prefill_T8192", "decode_T1", "decode_T8",
