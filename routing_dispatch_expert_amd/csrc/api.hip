@@ -585,7 +585,7 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
     if (e != hipSuccess) return MOE_ERR_HIP;
     // batches of a few tokens with internal routing: the gate/up decode launch
     // routes and dispatches them itself, one launch fewer
-    const bool fused = dec && !pre && P.T > 0 && P.T <= kFuseMaxT && Q <= kFuseMaxQ &&
+    const bool fused = dec && P.T > 0 && P.T <= kFuseMaxT && Q <= kFuseMaxQ &&
                        P.E <= kFuseMaxE && P.w_dtype == MOE_BF16;
     if (fused) {
         for (int st = MOE_STAGE_ROUTE; e == hipSuccess && st <= MOE_STAGE_SCATTER; ++st) e = mark(m, st, s);
@@ -634,6 +634,7 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
         DecodeFused fz = {};
         if (fused) {
             fz.logits = logits;
+            fz.ids_in = pre ? ids_in : nullptr;
             fz.bias = score_bias;
             fz.sigmoid = P.score_func == MOE_SIGMOID;
             fz.T = P.T;

@@ -151,14 +151,15 @@ struct DecodeSeg {
 };
 // Routing and dispatch done inside the gate/up launch for batches of at most
 // kFuseMaxT tokens and kFuseMaxQ routes over at most kFuseMaxE experts with
-// internal (softmax or sigmoid) routing: every workgroup computes the routes,
-// ranks, offsets and tile table into LDS and workgroup 0 writes the metadata
-// that later launches and the caller read.
+// internal (softmax or sigmoid) routing or preselected routes: every
+// workgroup computes the routes, ranks, offsets and tile table into LDS and
+// workgroup 0 writes the metadata that later launches and the caller read.
 constexpr int kFuseMaxT = 8;     // 32 tokens measured slower: each wavefront then routes 8 before its first weight load
 constexpr int kFuseMaxQ = 256;   // one 64-route step per wavefront of the launch
 constexpr int kFuseMaxE = 256;
 struct DecodeFused {
     const float* logits;    // [T, E]
+    const int32_t* ids_in;  // [T, k] preselected routes (then logits, ids and w are unused), or NULL
     const float* bias;      // [E] selection-only correction (sigmoid), or NULL
     int sigmoid;
     int T, k, E, ebits, C, renorm;

@@ -199,8 +199,10 @@ __device__ int32_t block_excl_scan_256(int32_t v, int32_t* s_w, int32_t& tot) {
 // the count kernel does), per-expert totals, exclusive scans of min(count, C)
 // and of the 32-row tile counts, then each kept route's row.  The offsets,
 // tile table and each row's route land in the kernel's LDS tables; workgroup 0
-// also writes ids, weights, counts, offsets, the tile table, row_src (rows
-// past the kept ones -1) and route_dst.  `scratch` (LDS, 4 E + T k ints) is
+// also writes ids, weights (when it routed), counts, offsets, the tile table,
+// row_src (rows past the kept ones -1) and route_dst.  Preselected routes are
+// read instead of routed; malformed ones are counted and marked as in the
+// count kernel.  `scratch` (LDS, 4 E + T k ints) is
 // free again on return.
 static_assert(kFuseMaxQ == kDWaves * kWave, "one 64-route rank step per wavefront");
 static_assert(kFuseMaxQ <= kDStageRows && kFuseMaxE <= 4 * kWave && kFuseMaxE <= kDecodeMaxGroups,
@@ -214,7 +216,9 @@ __device__ void fused_dispatch(const DecodeFused& f, int32_t* scratch, int32_t* 
     const int T = f.T, k = f.k, E = f.E, Q = T * k;
     int32_t* hist = scratch;            // [kDWaves][E]
     int32_t* sid = scratch + kDWaves * E;   // [Q]
-    {
+    if (f.ids_in != nullptr) {
+        for (int i = tid; i < Q; i += blockDim.x) sid[i] = f.ids_in[i];   // the caller's routes
+    } else {
         constexpr int TPW = kFuseMaxT / kDWaves;   // tokens per wavefront
         float v[TPW][4];
 #pragma unroll
