@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--dispatch", default="prefill_T2048,prefill_T8192,skewed_bf16",
                     help="comma-separated workloads whose moe_route / moe_dispatch (with the "
                          "x_disp row copy) are timed on their own ('' = none)")
+    ap.add_argument("--routing-modes", default="relu2_distinct_R1,relu2_shared_R1,relu2_distinct_R8,"
+                    "relu2_shared_R8,relu2_distinct_R16,relu2_shared_R16",
+                    help="workloads timed with internal routing and with the same routes "
+                         "preselected ('' = none)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
     ap.add_argument("--protocols", type=int, default=1,
@@ -246,6 +250,59 @@ def measure_dispatch(name, calls=50, min_warmup_s=MIN_WARMUP_S):
             "dispatch_GBps": round(gbps, 1), "dispatch_frac": round(gbps / HBM_PEAK_GBPS, 4),
             "route_us": round(out["route"], 2), "route_alg_bytes": rb,
             "route_GBps": round(rb / (out["route"] * 1e-6) / 1e9, 1)}
+
+
+def measure_routing_modes(name, steps=50, min_warmup_s=MIN_WARMUP_S):
+    """moe_forward of one workload with internal routing (logits in) and with
+    the same routes preselected (ids and weights in, taken from one internal
+    call beforehand): plain steps over one input bank, wall time per call."""
+    import torch
+    import routing_dispatch_expert_amd as rde
+    import synth
+
+    dev = "cuda:0"
+    cs = synth.case(name)
+    inp = synth.make_inputs(cs, dev)
+    p = rde.make_problem(cs.T, cs.H, cs.E, cs.k, cs.I, cs.C, cs.n_shared, cs.I_shared,
+                         act_dtype=cs.act_fmt, w_dtype=cs.w_fmt, act=cs.act,
+                         renormalize=cs.renormalize, score_func=cs.score_func,
+                         route_scale=cs.route_scale)
+    ws = torch.empty(rde.moe_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    rde.moe_workspace_init(ws)
+    adt = torch.float32 if cs.act_fmt == synth.FMT_F32 else torch.bfloat16
+    out = torch.empty((cs.T, cs.H), dtype=adt, device=dev)
+    ids = torch.empty((cs.T, cs.k), dtype=torch.int32, device=dev)
+    w = torch.empty((cs.T, cs.k), dtype=torch.float32, device=dev)
+    rde.moe_forward(p, inp.x, inp.logits, inp.score_bias, None, None, inp.w13, inp.w2, inp.s13,
+                    inp.s2, inp.w13_sh, inp.w2_sh, out, dict(ids=ids, w=w), ws)
+
+    def internal():
+        rde.moe_forward(p, inp.x, inp.logits, inp.score_bias, None, None, inp.w13, inp.w2, inp.s13,
+                        inp.s2, inp.w13_sh, inp.w2_sh, out, None, ws)
+
+    def preselected():
+        rde.moe_forward(p, inp.x, None, None, ids, w, inp.w13, inp.w2, inp.s13, inp.s2,
+                        inp.w13_sh, inp.w2_sh, out, None, ws)
+
+    res = {}
+    for label, fn in (("internal", internal), ("preselected", preselected)):
+        tw = time.perf_counter()
+        i = 0
+        while time.perf_counter() - tw < min_warmup_s:
+            fn()
+            i += 1
+            if i % 16 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        res[label] = (time.perf_counter() - t0) / steps * 1e6
+    if rde.moe_error(ws) != 0:
+        raise RuntimeError("malformed routes reported on synthetic inputs")
+    return {"internal_us": round(res["internal"], 2), "preselected_us": round(res["preselected"], 2),
+            "ratio": round(res["internal"] / res["preselected"], 3)}
 
 
 def measure_protocols(step, torch, groups=15, calls=20, graph_calls=64, graph_replays=10):
@@ -521,6 +578,13 @@ def main():
         torch.cuda.empty_cache()
     if sweep:
         line["sweep"] = sweep
+    modes = {}
+    for name in [s for s in args.routing_modes.split(",") if s]:
+        print(f"[bench] routing modes {name}", file=sys.stderr, flush=True)
+        modes[name] = measure_routing_modes(name)
+        torch.cuda.empty_cache()
+    if modes:
+        line["routing_modes"] = modes
     disp = {}
     for name in [s for s in args.dispatch.split(",") if s]:
         print(f"[bench] dispatch {name}", file=sys.stderr, flush=True)
