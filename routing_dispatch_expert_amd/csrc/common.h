@@ -154,7 +154,7 @@ struct DecodeSeg {
 // internal (softmax or sigmoid) routing or preselected routes: every
 // workgroup computes the routes, ranks, offsets and tile table into LDS and
 // workgroup 0 writes the metadata that later launches and the caller read.
-constexpr int kFuseMaxT = 8;     // 32 tokens measured slower: each wavefront then routes 8 before its first weight load
+constexpr int kFuseMaxT = 8;     // more tokens measured slower: the routing then delays the first weight load
 constexpr int kFuseMaxQ = 256;   // one 64-route step per wavefront of the launch
 constexpr int kFuseMaxE = 256;
 struct DecodeFused {

@@ -39,6 +39,8 @@
 // operands leaves the product unchanged), so each lane's bytes for a group
 // are one 64-byte run.  16-byte chunk c of row r sits at chunk slot
 // c ^ ((r ^ r >> 3) & 7): the fragment reads are free of bank conflicts.
+#include <type_traits>
+
 #include "route_wave.h"
 
 namespace rde {
@@ -219,29 +221,37 @@ __device__ void fused_dispatch(const DecodeFused& f, int32_t* scratch, int32_t* 
     if (f.ids_in != nullptr) {
         for (int i = tid; i < Q; i += blockDim.x) sid[i] = f.ids_in[i];   // the caller's routes
     } else {
-        constexpr int TPW = kFuseMaxT / kDWaves;   // tokens per wavefront
-        float v[TPW][4];
+        // experts per lane as in the other routing kernels (1, 2 or 4): the
+        // same wave routing, so the same weights
+        auto route_tokens = [&](auto epl_c) {
+            constexpr int EPL = decltype(epl_c)::value;
+            constexpr int TPW = kFuseMaxT / kDWaves;   // tokens per wavefront
+            float v[TPW][EPL];
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {   // all rows first: one memory latency
-            const int t = wv + kDWaves * i;
-            if (t < T) load_logits<4>(f.logits + (int64_t)t * E, E, lane, v[i]);
-        }
+            for (int i = 0; i < TPW; ++i) {   // all rows first: one memory latency
+                const int t = wv + kDWaves * i;
+                if (t < T) load_logits<EPL>(f.logits + (int64_t)t * E, E, lane, v[i]);
+            }
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int t = wv + kDWaves * i;
-            if (t >= T) break;   // wave-uniform
-            int id;
-            float wt;
-            if (f.sigmoid) route_row<4, true>(v[i], f.bias, E, k, f.renorm, f.scale, lane, id, wt);
-            else route_row<4, false>(v[i], nullptr, E, k, f.renorm, f.scale, lane, id, wt);
-            if (lane < k) {
-                sid[t * k + lane] = id;
-                if (writer) {
-                    f.ids[t * k + lane] = id;
-                    f.w[t * k + lane] = wt;
+            for (int i = 0; i < TPW; ++i) {
+                const int t = wv + kDWaves * i;
+                if (t >= T) break;   // wave-uniform
+                int id;
+                float wt;
+                if (f.sigmoid) route_row<EPL, true>(v[i], f.bias, E, k, f.renorm, f.scale, lane, id, wt);
+                else route_row<EPL, false>(v[i], nullptr, E, k, f.renorm, f.scale, lane, id, wt);
+                if (lane < k) {
+                    sid[t * k + lane] = id;
+                    if (writer) {
+                        f.ids[t * k + lane] = id;
+                        f.w[t * k + lane] = wt;
+                    }
                 }
             }
-        }
+        };
+        if (E <= kWave) route_tokens(std::integral_constant<int, 1>{});
+        else if (E <= 2 * kWave) route_tokens(std::integral_constant<int, 2>{});
+        else route_tokens(std::integral_constant<int, 4>{});
     }
     for (int i = tid; i < kDWaves * E; i += blockDim.x) hist[i] = 0;
     __syncthreads();
