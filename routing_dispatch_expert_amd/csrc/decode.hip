@@ -422,6 +422,21 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     const int64_t total = n0 + n1;
     const int64_t first = SPLIT ? blockIdx.x : (int64_t)wave * gridDim.x + blockIdx.x;
     const int64_t stride = SPLIT ? gridDim.x : (int64_t)gridDim.x * kDWaves;
+    // Position p of the loop (slot p % stride, round p / stride) -> unit.  When
+    // segment 1's units are longer (the shared experts' down projection runs
+    // over their concatenated intermediates), they go to slots that get one
+    // unit fewer than the others, in the first round; the routed units take
+    // the remaining positions in order.  A bijection on [0, total), the same
+    // in every workgroup.
+    const int64_t rounds = (total + stride - 1) / stride;
+    const int64_t full = total - (rounds - 1) * stride;   // slots with `rounds` units
+    const bool spread = n1 > 0 && d.n_seg > 1 && d.seg[1].K > d.seg[0].K && full < stride &&
+                        full + n1 <= stride && full <= n0;
+    auto unit_at = [&](int64_t p) -> int64_t {
+        if (!spread || p < full) return p;
+        if (p < full + n1) return n0 + (p - full);
+        return p - n1;
+    };
     unsigned char* ring = rings[wave];
     const uint32_t ring0 = __builtin_amdgcn_readfirstlane(lds_addr_d(ring));
     const int r32 = lane & 31, h = lane >> 5;
@@ -468,10 +483,11 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     };
     // item u: segment, expert (tile table), 32-row block, weight block
     auto make = [&](int64_t u, Item& it) {
-        it.u = u;
-        it.si = u < n0 ? 0 : 1;
+        it.u = u;                        // loop position
+        const int64_t un = unit_at(u);   // the unit it holds
+        it.si = un < n0 ? 0 : 1;
         const DecodeSeg& s = d.seg[it.si];
-        const int64_t lu = it.si == 0 ? u : u - n0;
+        const int64_t lu = it.si == 0 ? un : un - n0;
         const int ti = (int)(lu / s.blocks);
         it.blk = (int)(lu - (int64_t)ti * s.blocks);
         int m0;
