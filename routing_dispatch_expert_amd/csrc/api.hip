@@ -399,6 +399,8 @@ hipError_t run_decode(const DecodeSeg* a, const DecodeSeg* b, const int32_t* row
         kmin = std::min(kmin, g.K);
     }
     const int split = (units < (int64_t)decode_grid() * 4 && kmin >= 1280) ? 1 : 0;
+    // otherwise the partial last round is split the same way (same K bound)
+    d.tail_split = !split && kmin >= 1280;
     // the shared experts are always bf16; a segment list that starts with them
     // runs the bf16 instantiation
     const int small_m = (max_rows >= 0 && max_rows <= 8) ? 1 : 0;

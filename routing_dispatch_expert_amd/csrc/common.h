@@ -182,6 +182,7 @@ struct DecodeArgs {
     const float* route_w;
     int use_fused;          // segment 0's routes come from `fused`
     DecodeFused fused;
+    int tail_split;         // whole units in complete rounds, the last partial round split over a workgroup's wavefronts
 };
 // small_m: no group has more than 8 rows (the 8-row staging of the decode ring)
 hipError_t launch_decode_gemm(const DecodeArgs& d, int w_dtype, int split, int small_m, int grid,

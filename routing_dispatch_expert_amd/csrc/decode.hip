@@ -373,7 +373,7 @@ template <int EPI0, int EPI1, bool FP8, bool SPLIT, bool SMALLM, bool FUSED>
 __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs d) {
     using RG = DRing<SMALLM>;
     __shared__ __attribute__((aligned(1024))) unsigned char rings[kDWaves][kDRing];
-    __shared__ float red[SPLIT ? (kDWaves - 1) * 16 * 64 : 1];
+
     // wave index in a scalar register: the work item, and with it the segment
     // descriptor, is then wave-uniform (scalar loads, no vector-memory wait)
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -420,8 +420,22 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     const int64_t n0 = items(0);
     const int64_t n1 = d.n_seg > 1 ? items(1) : 0;
     const int64_t total = n0 + n1;
+    // Positions: SPLIT takes one unit per workgroup at a time (position b + G r
+    // for workgroup b), its wavefronts splitting the unit's K.  Otherwise every
+    // wavefront takes whole units (position w G + b + 4 G r for wavefront w),
+    // and with tail_split only the complete rounds may run that way: the last,
+    // partial round (positions from tail0) is then taken one unit per
+    // workgroup and split, so that a fraction of the wavefronts do not each
+    // stream one more whole unit while the others wait.
+    // Used when there is at least one complete round and the partial one
+    // holds at most one unit per workgroup: larger tails cost each split unit
+    // its own ring fill and measured slower.
+    const int64_t WA = (int64_t)gridDim.x * kDWaves;
+    const bool hybrid = !SPLIT && d.tail_split && total >= WA && total % WA != 0 &&
+                        total % WA <= (int64_t)gridDim.x;
+    const int64_t tail0 = hybrid ? (total / WA) * WA : total;
     const int64_t first = SPLIT ? blockIdx.x : (int64_t)wave * gridDim.x + blockIdx.x;
-    const int64_t stride = SPLIT ? gridDim.x : (int64_t)gridDim.x * kDWaves;
+    const int64_t stride = SPLIT ? gridDim.x : WA;
     // Position p of the loop (slot p % stride, round p / stride) -> unit.  When
     // segment 1's units are longer (the shared experts' down projection runs
     // over their concatenated intermediates), they go to slots that get one
@@ -430,8 +444,8 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     // in every workgroup.
     const int64_t rounds = (total + stride - 1) / stride;
     const int64_t full = total - (rounds - 1) * stride;   // slots with `rounds` units
-    const bool spread = n1 > 0 && d.n_seg > 1 && d.seg[1].K > d.seg[0].K && full < stride &&
-                        full + n1 <= stride && full <= n0;
+    const bool spread = !hybrid && n1 > 0 && d.n_seg > 1 && d.seg[1].K > d.seg[0].K &&
+                        full < stride && full + n1 <= stride && full <= n0;
     auto unit_at = [&](int64_t p) -> int64_t {
         if (!spread || p < full) return p;
         if (p < full + n1) return n0 + (p - full);
@@ -443,13 +457,14 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     const int dr = lane >> 3, dsl = lane & 7;   // DMA: instruction i covers rows 8i + lane/8, chunk slot lane%8
 
     // this wavefront's K range and DMA sources of the item's block m0
-    auto setup = [&](Item& it, int m0) {
+    // spl: the unit is split over the workgroup's wavefronts
+    auto setup = [&](Item& it, int m0, bool spl) {
         const DecodeSeg& s = d.seg[it.si];
         it.m0 = m0;
         it.mrows = min(kDecodeBM, it.rows - m0);
         const int nKall = s.K / kDGroupK;
-        const int kq = SPLIT ? (nKall + kDWaves - 1) / kDWaves : nKall;
-        it.g0 = SPLIT ? min(nKall, wave * kq) : 0;
+        const int kq = spl ? (nKall + kDWaves - 1) / kDWaves : nKall;
+        it.g0 = spl ? min(nKall, wave * kq) : 0;
         it.nK = min(nKall, it.g0 + kq) - it.g0;
         // units running at the same time start at different K groups, so the
         // weight rows (a power-of-two stride apart) are not all read at the
@@ -482,7 +497,7 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
         }
     };
     // item u: segment, expert (tile table), 32-row block, weight block
-    auto make = [&](int64_t u, Item& it) {
+    auto make = [&](int64_t u, Item& it, bool spl) {
         it.u = u;                        // loop position
         const int64_t un = unit_at(u);   // the unit it holds
         it.si = un < n0 ? 0 : 1;
@@ -504,7 +519,7 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
             it.base = 0;
             it.rows = s.uniform_rows;
         }
-        setup(it, m0);
+        setup(it, m0, spl);
         if ((it.si == 0 ? EPI0 : EPI1) == EPI_COMBINE) {
             const int m = min(lane & 31, it.mrows - 1);
             const int rr = it.base + m0 + m;
@@ -534,78 +549,114 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
             dma16_d(it.bsrc[i] + kb * (fp8 ? 1 : 2), __builtin_amdgcn_readfirstlane(st + RG::A_BYTES + i * 1024));
     };
 
-    Item cur, nxt;
-    if (first >= total) return;   // SPLIT: the same for every wavefront of the workgroup
-    make(first, cur);
-    int issued = 0, consumed = 0;  // stages of this wavefront's stream
-    int pre = 0;                   // stages of `cur` already issued
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    while (true) {
-        for (; pre < min(RG::NST - 1, cur.nK); ++pre) issue(cur, pre, (issued++) % RG::NST);
-        const bool has_next = cur.u + stride < total;
-        const bool cur_fp8 = FP8 && cur.si == 0;
+    // The loop, once for launches that split their partial last round
+    // (HYB: whether the current unit is split is a run-time state) and once
+    // for the others (fixed by SPLIT); `hybrid` is workgroup-uniform.
+    auto run = [&](auto hyb_c) {
+        constexpr bool HYB = decltype(hyb_c)::value;
+        Item cur, nxt;
+        // the phase-1 positions of every wavefront of a workgroup are equally many,
+        // and the phase-2 positions are the workgroup's: both tests are
+        // workgroup-uniform where it matters (SPLIT, and the switch to phase 2)
+        bool sp = SPLIT;   // (HYB) the current unit is split over the workgroup's wavefronts
+        int64_t pstride = stride, pend = SPLIT ? total : tail0;
+        int64_t p0 = first;
+        if (p0 >= pend) {
+            if (!HYB || tail0 + blockIdx.x >= total) return;
+            sp = true;
+            p0 = tail0 + blockIdx.x;
+            pstride = gridDim.x;
+            pend = total;
+        }
+        make(p0, cur, HYB ? sp : SPLIT);
+        int issued = 0, consumed = 0;  // stages of this wavefront's stream
+        int pre = 0;                   // stages of `cur` already issued
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        while (true) {
+            for (; pre < min(RG::NST - 1, cur.nK); ++pre) issue(cur, pre, (issued++) % RG::NST);
+            int64_t pn = cur.u + pstride;
+            bool has_next = pn < pend;
+            if (HYB && !has_next && !sp && tail0 + blockIdx.x < total) {
+                has_next = true;   // then the workgroup's share of the partial round
+                pn = tail0 + blockIdx.x;
+            }
+            const bool cur_fp8 = FP8 && cur.si == 0;
 
-        f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-        for (int gk = 0; gk < cur.nK; ++gk) {
-            wait_stages<RG::PER>(min(RG::NST - 2, cur.nK - 1 - gk));
-            const unsigned char* sa = ring + (consumed % RG::NST) * RG::STAGE;
-            const unsigned char* sb = sa + RG::A_BYTES;
-            const int ra = SMALLM ? (r32 & 7) : r32;   // activation row of this lane's fragment
-            bf16x8 af[4], bfr[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = 4 * h + j;
-                af[j] = *(const bf16x8*)(sa + ra * 128 + ((c ^ dswz(ra)) * 16));
-                if (cur_fp8) {
-                    // 8 e4m3 codes at byte (32h + 8j) of the 64-byte row group
-                    const int byte = 32 * h + 8 * j;
-                    const int cc = byte >> 4;
-                    bfr[j] = e4m3x8_to_bf16x8(*(const uint2*)(sb + r32 * 128 + ((cc ^ dswz(r32)) * 16) + (byte & 15)));
-                } else {
-                    bfr[j] = *(const bf16x8*)(sb + r32 * 128 + ((c ^ dswz(r32)) * 16));
+            f32x16 acc;
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+            for (int gk = 0; gk < cur.nK; ++gk) {
+                wait_stages<RG::PER>(min(RG::NST - 2, cur.nK - 1 - gk));
+                const unsigned char* sa = ring + (consumed % RG::NST) * RG::STAGE;
+                const unsigned char* sb = sa + RG::A_BYTES;
+                const int ra = SMALLM ? (r32 & 7) : r32;   // activation row of this lane's fragment
+                bf16x8 af[4], bfr[4];
+    #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = 4 * h + j;
+                    af[j] = *(const bf16x8*)(sa + ra * 128 + ((c ^ dswz(ra)) * 16));
+                    if (cur_fp8) {
+                        // 8 e4m3 codes at byte (32h + 8j) of the 64-byte row group
+                        const int byte = 32 * h + 8 * j;
+                        const int cc = byte >> 4;
+                        bfr[j] = e4m3x8_to_bf16x8(*(const uint2*)(sb + r32 * 128 + ((cc ^ dswz(r32)) * 16) + (byte & 15)));
+                    } else {
+                        bfr[j] = *(const bf16x8*)(sb + r32 * 128 + ((c ^ dswz(r32)) * 16));
+                    }
                 }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage read before it is refilled
+                ++consumed;
+                const int s3 = gk + RG::NST - 1;
+                if (s3 < cur.nK) issue(cur, s3, (issued++) % RG::NST);
+    #pragma unroll
+                for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[j], acc, 0, 0, 0);
             }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage read before it is refilled
-            ++consumed;
-            const int s3 = gk + RG::NST - 1;
-            if (s3 < cur.nK) issue(cur, s3, (issued++) % RG::NST);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[j], acc, 0, 0, 0);
-        }
 
-        // ---- sum the wavefronts' K shares in a fixed order (wave 0 first) ----
-        bool owner = true;
-        if (SPLIT) {
-            if (wave > 0) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) red[((wave - 1) * 16 + r) * 64 + lane] = acc[r];
+            // ---- sum the wavefronts' K shares in a fixed order (wave 0 first) ----
+            // Each wavefront's ring is idle here (its stages are all consumed), so
+            // it holds the wavefront's partial sums; the second barrier keeps the
+            // rings from being refilled before wavefront 0 has read them.
+            bool owner = true;
+            if (HYB ? sp : SPLIT) {
+                if (wave > 0) {
+                    float* mine = (float*)ring;
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) mine[r * 64 + lane] = acc[r];
+                }
+                __syncthreads();
+                if (wave == 0) {
+    #pragma unroll
+                    for (int w = 1; w < kDWaves; ++w) {
+                        const float* theirs = (const float*)rings[w];
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[r] += theirs[r * 64 + lane];
+                    }
+                }
+                __syncthreads();
+                owner = wave == 0;
             }
-            __syncthreads();
-            if (wave == 0) {
-#pragma unroll
-                for (int w = 1; w < kDWaves; ++w)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[r] += red[((w - 1) * 16 + r) * 64 + lane];
+            if (owner) {
+                if (cur.si == 0)
+                    epilogue<EPI0, FP8>(d.seg[0], cur.group, cur.blk, cur.m0, cur.mrows, cur.base, cur.q, cur.cw, acc, lane);
+                else
+                    epilogue<EPI1, false>(d.seg[1], cur.group, cur.blk, cur.m0, cur.mrows, cur.base, cur.q, cur.cw, acc, lane);
             }
-            __syncthreads();
-            owner = wave == 0;
+            if (!has_next) break;
+            // the next item is set up with nothing of this wavefront's ring in
+            // flight: its lookups (row gather, combine weights) are plain loads
+            // whose waits would otherwise drain the ring
+            if (HYB && !sp && pn >= tail0) {
+                sp = true;
+                pstride = gridDim.x;
+                pend = total;
+            }
+            make(pn, nxt, HYB ? sp : SPLIT);
+            cur = nxt;
+            pre = 0;
         }
-        if (owner) {
-            if (cur.si == 0)
-                epilogue<EPI0, FP8>(d.seg[0], cur.group, cur.blk, cur.m0, cur.mrows, cur.base, cur.q, cur.cw, acc, lane);
-            else
-                epilogue<EPI1, false>(d.seg[1], cur.group, cur.blk, cur.m0, cur.mrows, cur.base, cur.q, cur.cw, acc, lane);
-        }
-        if (!has_next) break;
-        // the next item is set up with nothing of this wavefront's ring in
-        // flight: its lookups (row gather, combine weights) are plain loads
-        // whose waits would otherwise drain the ring
-        make(cur.u + stride, nxt);
-        cur = nxt;
-        pre = 0;
-    }
+    };
+    if (hybrid) run(std::true_type{});
+    else run(std::false_type{});
 }
 
 }  // namespace
