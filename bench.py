@@ -15,6 +15,7 @@ on a bounded sample of the same workload.
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -27,6 +28,7 @@ HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 N_BANKS = 4                  # rotating x / logits banks
 MIN_WARMUP_S = 0.2           # shortest warm-up of a sweep workload
+SWEEP_MIN_TIMED_S = 0.02     # shortest plain timed region of a sweep workload
 
 
 def parse():
@@ -82,7 +84,8 @@ def stage_bytes_flops(cs, R, touched, ab, wb):
     return st
 
 
-def run_workload(name, steps, warmup, with_events=True, protocols=False, min_warmup_s=0.0):
+def run_workload(name, steps, warmup, with_events=True, protocols=False, min_warmup_s=0.0,
+                 min_timed_s=0.0, graph=False):
     import torch
     import routing_dispatch_expert_amd as rde
     import synth
@@ -130,9 +133,15 @@ def run_workload(name, steps, warmup, with_events=True, protocols=False, min_war
         if i % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    # timed region 1: plain steps (the throughput figure)
+    # timed region 1: plain steps (the throughput figure), at least
+    # min_timed_s of them at the warm-up's rate, so that the synchronisations
+    # bracketing the region stay small against it
+    n_plain = steps
+    if min_timed_s > 0 and i > 0:
+        per_step = (time.perf_counter() - tw) / i
+        n_plain = max(steps, int(math.ceil(min_timed_s / per_step)))
     t0 = time.perf_counter()
-    for i in range(steps):
+    for i in range(n_plain):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -147,6 +156,7 @@ def run_workload(name, steps, warmup, with_events=True, protocols=False, min_war
         torch.cuda.synchronize()
         wall_ev = time.perf_counter() - t0
     proto = measure_protocols(step, torch) if protocols else None
+    graph_us = measure_graph(step, torch) if graph else None
     if rde.moe_error(ws) != 0:
         raise RuntimeError("malformed routes reported on synthetic inputs")
     stages = {}
@@ -160,8 +170,9 @@ def run_workload(name, steps, warmup, with_events=True, protocols=False, min_war
     touched = sum(1 for e in range(cs.E) if off[e + 1] > off[e])
     ab = 4 if cs.act_fmt == synth.FMT_F32 else 2
     wb = {synth.FMT_F32: 4, synth.FMT_BF16: 2, synth.FMT_E4M3: 1}[cs.w_fmt]
-    return dict(cs=cs, steps=steps, wall=wall, wall_ev=wall_ev, stages=stages, R=R, touched=touched,
-                bf=stage_bytes_flops(cs, R, touched, ab, wb), base=base, protocols=proto)
+    return dict(cs=cs, steps=steps, n_plain=n_plain, wall=wall, wall_ev=wall_ev, stages=stages, R=R,
+                touched=touched, bf=stage_bytes_flops(cs, R, touched, ab, wb), base=base,
+                protocols=proto, graph_us=graph_us)
 
 
 def dispatch_bytes(cs, R):
@@ -305,6 +316,27 @@ def measure_routing_modes(name, steps=50, min_warmup_s=MIN_WARMUP_S):
             "ratio": round(res["internal"] / res["preselected"], 3)}
 
 
+def measure_graph(step, torch, graph_calls=64, graph_replays=10):
+    """us per call of graph_calls back-to-back calls, rotating over the input
+    banks, captured once into a HIP graph and replayed: the host's launch
+    cost is paid once per replay, not per call."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(graph_calls):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(graph_replays):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / (graph_replays * graph_calls) * 1e6
+
+
 def measure_protocols(step, torch, groups=15, calls=20, graph_calls=64, graph_replays=10):
     """Two further views of the same call.
     cold: a 1 GiB device write before every call evicts L2 and the 256 MB
@@ -326,21 +358,7 @@ def measure_protocols(step, torch, groups=15, calls=20, graph_calls=64, graph_re
         cold += [e0[c].elapsed_time(e1[c]) * 1e3 for c in range(calls)]
     del flush
     cold.sort()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=side):
-        for i in range(graph_calls):
-            step(i)
-    torch.cuda.current_stream().wait_stream(side)
-    for _ in range(2):
-        g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(graph_replays):
-        g.replay()
-    torch.cuda.synchronize()
-    per_call = (time.perf_counter() - t0) / (graph_replays * graph_calls)
+    per_call = measure_graph(step, torch, graph_calls, graph_replays) * 1e-6
     return {"cold_us_median": round(cold[len(cold) // 2], 2),
             "cold_us_p95": round(cold[int(len(cold) * 0.95)], 2),
             "cold_samples": f"{groups} x {calls} calls, a 1 GiB device write before each",
@@ -426,7 +444,7 @@ def layer_roofline(res, copy_gbps=None):
     HBM peak, flops / bf16 MFMA peak); `frac_copy` takes the measured device
     copy bandwidth in place of the HBM peak."""
     byts, flops = layer_work(res["cs"], res["R"], res["touched"])
-    t_meas = res["wall"] / res["steps"]
+    t_meas = res["wall"] / res.get("n_plain", res["steps"])
     t_h, t_m = byts / (HBM_PEAK_GBPS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
     out = {"alg_bytes": byts, "alg_flops": flops, "t_hbm_us": round(t_h * 1e6, 2),
            "t_mfma_us": round(t_m * 1e6, 2), "bound": "mfma" if t_m > t_h else "hbm",
@@ -463,7 +481,7 @@ def summary(res, copy_gbps=None):
     g_us = st["gemm1"] + st["gemm2"]
     g_fl = bf["gemm1"][1] + bf["gemm2"][1]
     return {
-        "us_per_layer": round(res["wall"] / res["steps"] * 1e6, 2),
+        "us_per_layer": round(res["wall"] / res.get("n_plain", res["steps"]) * 1e6, 2),
         "sum_of_stage_us": round(sum(st.values()), 2),
         "dispatch_us": round(disp_us, 2),
         "dispatch_bytes": disp_b,
@@ -532,7 +550,7 @@ def main():
     res = run_workload(args.workload, args.steps, args.warmup, protocols=bool(args.protocols))
     copy_gbps = measure_copy_gbps(torch) if args.protocols else None
     cs = res["cs"]
-    ms = res["wall"] / args.steps * 1e3
+    ms = res["wall"] / res["n_plain"] * 1e3
     summ = summary(res, copy_gbps)
     dom = dominant_gemm(res)
     line = {
@@ -566,11 +584,14 @@ def main():
     sweep = {}
     for name in [s for s in args.sweep.split(",") if s]:
         print(f"[bench] sweep {name}", file=sys.stderr, flush=True)
-        r2 = run_workload(name, max(5, args.steps // 3), 10, min_warmup_s=MIN_WARMUP_S)
-        ms2 = r2["wall"] / max(5, args.steps // 3) * 1e3
+        r2 = run_workload(name, max(5, args.steps // 3), 10, min_warmup_s=MIN_WARMUP_S,
+                          min_timed_s=SWEEP_MIN_TIMED_S, graph=True)
+        ms2 = r2["wall"] / r2["n_plain"] * 1e3
         sw = summary(r2, copy_gbps)
         sw["tokens_per_s"] = round(r2["cs"].T / (ms2 * 1e-3), 1)
         sw["ms_per_step"] = round(ms2, 4)
+        sw["steps"] = r2["n_plain"]
+        sw["graph_us_per_call"] = round(r2["graph_us"], 2)
         d2 = dominant_gemm(r2)
         sw["roofline"] = roofline_of(r2, d2)
         sweep[name] = sw

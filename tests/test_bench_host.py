@@ -71,3 +71,13 @@ def test_forward_scatter_bytes_are_metadata_only_for_bf16():
     f32 = synth.case("tiny_fp32")
     bf32 = bench.stage_bytes_flops(f32, 128, 16, 4, 4)
     assert bf32["scatter"][0] == 64 * 256 * 4 + 128 * 256 * 4 + 128 * 16 + 128 * 4
+
+
+def test_layer_roofline_divides_by_the_plain_step_count():
+    # a sweep workload times more plain steps than event-timed ones: the
+    # plain wall time is divided by its own step count
+    cs = synth.case("prefill_T8192")
+    a = bench.layer_roofline({"cs": cs, "R": 65536, "touched": 128, "wall": 2e-3, "steps": 2})
+    b = bench.layer_roofline({"cs": cs, "R": 65536, "touched": 128, "wall": 8e-3, "steps": 2,
+                              "n_plain": 8})
+    assert a["frac"] == pytest.approx(b["frac"])
