@@ -365,6 +365,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     for (int st = 0; st < STG - 1; ++st) issue(cur, st, st);   // nk >= STG - 1 (K >= 128)
 
     const int rA = lane & 31, half = lane >> 5;
+    // This lane's fragment rows are rA plus multiples of 32, and swz depends on
+    // bits 1..3 of the row only: every row block shares the swizzle of rA, so
+    // two per-lane byte offsets (logical chunk half, and 2 + half) serve all
+    // of them, and the blocks differ by compile-time constants.
+    const int zr = swz(rA);
+    const int loff0 = rA * 64 + ((half ^ zr) * 16), loff1 = rA * 64 + (((2 + half) ^ zr) * 16);
     for (; Lt < total; Lt += G) {
         const bool has_next = Lt + G < total;
         const Tile nxt = has_next ? make_tile(Lt + G) : cur;
@@ -425,22 +431,21 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
                     // this lane's k = 16 ks + 8 half .. + 7: logical 16-byte chunk c
                     // of the 64-byte A half ks / 2 and of a bf16 B row; in an e4m3
                     // B row, the 8-byte piece `half` of chunk ks
-                    const int c = (ks & 1) * 2 + half;
+                    const int lo = (ks & 1) ? loff1 : loff0;   // chunk c = 2 (ks & 1) + half
                     const unsigned char* sa = sA[slot] + (ks >> 1) * A_STAGE;
                     bf16x8 bv[NBW], av[NA > 0 ? NA : 1];
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb) {
-                        const int r = wn * BW + nb * 32 + rA;
+                        const int r0 = wn * BW + nb * 32;   // row rA of this block: r0 + rA
                         if (FP8) {
-                            bv[nb] = e4m3x8_to_bf16x8(*(const uint2*)(sb + r * 64 + ((ks ^ swz(r)) * 16) + half * 8));
+                            bv[nb] = e4m3x8_to_bf16x8(*(const uint2*)(sb + (r0 + rA) * 64 + ((ks ^ zr) * 16) + half * 8));
                         } else {
-                            bv[nb] = *(const bf16x8*)(sb + r * 64 + ((c ^ swz(r)) * 16));
+                            bv[nb] = *(const bf16x8*)(sb + r0 * 64 + lo);
                         }
                     }
 #pragma unroll
                     for (int mb = 0; mb < NA; ++mb) {
-                        const int ra = (wm + 2 * mb) * 32 + rA;
-                        av[mb] = *(const bf16x8*)(sa + ra * 64 + ((c ^ swz(ra)) * 16));
+                        av[mb] = *(const bf16x8*)(sa + (wm + 2 * mb) * 32 * 64 + lo);
                     }
 #pragma unroll
                     for (int mb = 0; mb < NA; ++mb)
