@@ -63,6 +63,12 @@ SMALL = {
     "sigmoid_prefill_small": ("sigmoid_T2048", dict(T=300, H=256, E=16, k=4, I=256, C=300)),
     # sigmoid routing inside the gate/up decode launch (8 tokens, 240 experts)
     "sigmoid_decode_fused": ("sigmoid_relu2_R16", dict(T=8, H=256, I=256, C=8)),
+    # more than 8 (and 16) slots per token with capacity drops: the combine
+    # loads a token's rows 8 slots at a time, and dropped slots fall in every
+    # batch; tiled path, slot-indexed decode path, float32 combine
+    "k20_capacity_prefill": ("prefill_T256", dict(T=300, H=256, E=32, k=20, I=128, C=60)),
+    "k20_capacity_decode": ("decode_T8", dict(T=24, H=256, E=64, k=20, I=128, I_shared=128, C=3)),
+    "k12_capacity_fp32": ("tiny_fp32", dict(k=12, C=20)),
 }
 # Full-size workloads.
 FULL = ["tiny_fp32", "prefill_T256", "prefill_T2048", "prefill_T8192", "decode_T1", "decode_T8",
