@@ -25,6 +25,13 @@ in float32 with torch's generator on the requested device and rounded to
 bf16 (round-to-nearest-even) where the case is bf16.  fp8 weights are
 quantised per output row at generation time: scale = max|w| / 448 and the
 code is the OCP e4m3fn value nearest to w / scale.
+
+Two value scales.  The workloads' own scale draws x and every weight from
+N(0, 0.02^2) (the benchmark inputs).  `unit_scale` gives the same shapes and
+routes with x ~ N(0, 1) and each weight matrix drawn N(0, 1/K) for its input
+width K (H for w13, I for w2), so every layer output is O(1): a comparison
+against the oracle with an absolute floor of 1e-3 then measures the kernel,
+not the floor.
 """
 from __future__ import annotations
 
@@ -73,6 +80,7 @@ class Case:
     zipf_s: float = 1.1
     w_std: float = 0.02
     x_std: float = 0.02
+    fan_in: bool = False               # weights N(0, 1/K) for input width K (w_std unused)
     seed: int = 0
 
     @property
@@ -128,6 +136,13 @@ def case(name: str, **over) -> Case:
     sizes in tests: same structure, fewer tokens or experts)."""
     base = CASES[name]
     return replace(base, **over) if over else base
+
+
+def unit_scale(cs: Case) -> Case:
+    """The same workload with O(1) outputs: x ~ N(0, 1), w13 ~ N(0, 1/H),
+    w2 ~ N(0, 1/I) (shared experts: 1/H and 1/I_shared); e4m3 weights are
+    quantised from those."""
+    return replace(cs, x_std=1.0, fan_in=True)
 
 
 def _gen(seed: int, tensor: str, expert: int, device) -> torch.Generator:
@@ -197,8 +212,10 @@ def make_expert_weights(cs: Case, e: int, device="cpu", shared: bool = False):
     I = cs.I_shared if shared else cs.I
     rows = 2 * I if (shared or cs.act == ACT_SWIGLU) else I
     t13, t2 = ("w13_sh", "w2_sh") if shared else ("w13", "w2")
-    a = _normal((rows, cs.H), cs.w_std, cs.seed, t13, e, device)
-    b = _normal((cs.H, I), cs.w_std, cs.seed, t2, e, device)
+    std13 = 1.0 / math.sqrt(cs.H) if cs.fan_in else cs.w_std
+    std2 = 1.0 / math.sqrt(I) if cs.fan_in else cs.w_std
+    a = _normal((rows, cs.H), std13, cs.seed, t13, e, device)
+    b = _normal((cs.H, I), std2, cs.seed, t2, e, device)
     if cs.w_fmt == FMT_E4M3 and not shared:
         q13, s13 = _quant_e4m3_rows(a)
         q2, s2 = _quant_e4m3_rows(b)
@@ -280,3 +297,77 @@ def bad_routes(T: int, k: int, E: int, kind: str, seed: int = 0) -> torch.Tensor
     elif kind != "none":
         raise ValueError(kind)
     return ids
+
+
+def cancellation_inputs(T: int, H: int, E: int, k: int, I: int, act: int, device="cpu",
+                        seed: int = 0) -> Inputs:
+    """Large terms that cancel across K tiles, with unit terms kept apart.
+
+    The cancellation regression of "Extend MoEPacked for Bolt ReLU-square
+    routing and BF16 IQ2 precision" (PR 33963, "Motivation and Context" and
+    the commit that keeps unit contributions outside large-magnitude
+    tensor-core partials) separates results that differ only in how large
+    partial sums absorb unit terms.  Here every product is an integer (or, in
+    the second SwiGLU projection, a bf16 value of modest size) and every
+    partial sum stays below 2^24, so the exact result does not depend on the
+    order in which K is summed, inside an MFMA or across K tiles:
+
+      x[t, p+] = x[t, p-] = 2^10 and w13[e, i, p+] = 2^10, w13[e, i, p-] = -2^10
+        on every row i: the two 2^20 products cancel; p+ lies in the first
+        64-wide K block, p- in the last;
+      x[t, pb] = 8 and w13[e, i, pb] = 8 (ReLU-square, or the gate and up
+        rows of SwiGLU) only on two rows b1 < b2 of each expert, which then
+        carry 64 + (unit terms), i.e. h ~ 64^2 (ReLU-square) or ~ 12^2-sized
+        values for SwiGLU (there pb gets 3.5 and 3.5, see below);
+      w2[e, o, b1] = +L2, w2[e, o, b2] = -L2 with h[b1] = h[b2] (identical
+        rows), so the down projection's large terms cancel too; b1 lies in
+        the first K block of I, b2 in the last;
+      unit terms: x in {0, 1} and weights in {-1, 0, 1}, sparse, only in
+        16-wide K chunks that hold none of the large positions.
+
+    Logits are +16 on k experts per token ((t + j) mod E) and -16 elsewhere,
+    so with k in {1, 2, 4, 8} every weight is exactly 1/k.  ReLU-square
+    results are exact integers (or halves, quarters ...) on both sides; SwiGLU
+    results differ only by the rounding of silu.  bf16 storage throughout."""
+    if H % 64 or I % 64 or H < 128 or I < 128:
+        raise ValueError("H and I must be multiples of 64, at least 128")
+    g = torch.Generator().manual_seed(seed * 7919 + 101)
+    p_plus, p_minus, p_big = 3, H - 5, H // 2 + 1
+    b1, b2 = 2, I - 3
+    big_cols = {p_plus // 16, p_minus // 16, p_big // 16}
+    unit_k = torch.tensor([c // 16 not in big_cols for c in range(H)])
+    unit_i = torch.tensor([c // 16 not in {b1 // 16, b2 // 16} for c in range(I)])
+
+    x = (torch.rand((T, H), generator=g) < 0.125).float() * unit_k
+    x[:, p_plus] = 1024.0
+    x[:, p_minus] = 1024.0
+    x[:, p_big] = 8.0 if act == ACT_RELU2 else 3.5
+
+    def sparse_pm1(shape, density):
+        r = torch.rand(shape, generator=g)
+        s = torch.where(torch.rand(shape, generator=g) < 0.5, -1.0, 1.0)
+        return (r < density).float() * s
+
+    rows = 2 * I if act == ACT_SWIGLU else I
+    w13 = sparse_pm1((E, rows, H), 1.0 / 16) * unit_k
+    w13[:, :, p_plus] = 1024.0
+    w13[:, :, p_minus] = -1024.0
+    big_rows = [b1, b2] + ([I + b1, I + b2] if act == ACT_SWIGLU else [])
+    # identical rows b1 / b2 (and their up rows): equal h, exact cancellation
+    w13[:, b2] = w13[:, b1]
+    if act == ACT_SWIGLU:
+        w13[:, I + b2] = w13[:, I + b1]
+    for r in big_rows:
+        w13[:, r, p_big] = 8.0 if act == ACT_RELU2 else 3.5
+    w2 = sparse_pm1((E, H, I), 1.0 / 8) * unit_i
+    L2 = 1024.0 if act == ACT_RELU2 else 32.0
+    w2[:, :, b1] = L2
+    w2[:, :, b2] = -L2
+
+    lg = torch.full((T, E), -16.0)
+    for t in range(T):
+        for j in range(k):
+            lg[t, (t + j) % E] = 16.0
+    cs = Case("cancellation", T=T, H=H, E=E, k=k, I=I, C=T, act=act)
+    bf = lambda t: t.to(torch.bfloat16).to(device)
+    return Inputs(cs, bf(x), lg.to(device), bf(w13), bf(w2))

@@ -6,8 +6,16 @@ come from the oracle only.  Tolerances are the layer's contract:
   bf16 tensors: max|d| <= 1e-2 * max|ref| + 1e-3
   fp32 tensors: max|d| <= 1e-5 * max|ref|
   ids, counts, offsets, row_src, route_dst, x_disp: bit-exact
+
+A bf16 comparison is only accepted where it can fail: with outputs far below
+the 1e-3 floor an all-zero result would pass, so `assert_bf16_close` refuses
+any reference whose floor exceeds 2.5 % of max|ref| (then a result off by 5 %
+of max|ref| always fails).  Parity cases therefore run on `synth.unit_scale`
+inputs, whose outputs are O(1).
 """
 from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -17,6 +25,31 @@ import routing_dispatch_expert_amd as rde
 import synth
 
 DEV = "cuda:0"
+BF16_REL, BF16_FLOOR = 1e-2, 1e-3
+# largest accepted floor / max|ref|: a 5 % error then exceeds 1 % + 2.5 %
+MAX_FLOOR_FRACTION = 0.025
+ORACLE_THREADS = 12
+
+
+def parity_case(name: str, **over) -> synth.Case:
+    """A named workload (optionally reduced) at the unit value scale."""
+    return synth.unit_scale(synth.case(name, **over))
+
+
+class VacuousComparison(AssertionError):
+    """The reference is so small that the tolerance floor alone covers it."""
+
+
+def bf16_tolerance(ref: np.ndarray) -> float:
+    """max|d| allowed for a bf16 tensor: 1e-2 * max|ref| + 1e-3, refused
+    (VacuousComparison) where the 1e-3 floor exceeds 2.5 % of max|ref|."""
+    ref = np.asarray(ref, np.float64)
+    fin = np.isfinite(ref)
+    m = float(np.abs(ref[fin]).max()) if fin.any() else 0.0
+    if BF16_FLOOR > MAX_FLOOR_FRACTION * m:
+        raise VacuousComparison(f"max|ref| = {m:.3e}: the floor {BF16_FLOOR:g} alone would "
+                                f"accept an all-zero result")
+    return BF16_REL * m + BF16_FLOOR
 
 
 def problem(cs: synth.Case) -> rde.moe_problem:
@@ -51,8 +84,8 @@ def assert_bf16_close(got: torch.Tensor, ref: np.ndarray, what=""):
     fin = np.isfinite(ref)
     if not fin.any():
         return
+    tol = bf16_tolerance(ref)
     d = np.abs(g[fin] - ref[fin]).max()
-    tol = 1e-2 * np.abs(ref[fin]).max() + 1e-3
     assert d <= tol, f"{what}: max|d| = {d:.3e} > {tol:.3e}"
 
 
@@ -88,32 +121,42 @@ def host_expert(inp_dev: synth.Inputs, e: int):
     return cv(inp_dev.w13[e]), cv(inp_dev.w2[e]), s13, s2
 
 
+def parallel_map(fn, items):
+    """fn over items on a few host threads (the oracle's C calls release the
+    GIL; each call is itself single-threaded)."""
+    with ThreadPoolExecutor(ORACLE_THREADS) as ex:
+        return list(ex.map(fn, items))
+
+
 def oracle_token_rows(cs, inp_dev, x_host, ids, w, route_dst, tokens, y_shared_host=None):
     """Oracle outputs of the given tokens (float64 [len, H]) from the oracle's
     own routing (ids, w) and dispatch (route_dst), computing only the experts
-    those tokens use."""
-    cache = {}
-    ys = []
-    for t in tokens:
-        acc_rows = np.zeros((1, cs.H))
-        y_rows = []
+    those tokens use: every expert's rows in one oracle call, experts on
+    several host threads."""
+    tokens = list(tokens)
+    uses = {}
+    for i, t in enumerate(tokens):
         for j in range(cs.k):
-            if route_dst[t, j] < 0:
-                y_rows.append(np.zeros((1, cs.H)))
-                continue
-            e = int(ids[t, j])
-            if e not in cache:
-                cache[e] = host_expert(inp_dev, e)
-            a, b, sa, sb = cache[e]
-            y_rows.append(oracle.expert_rows(x_host[t:t + 1], a, b, cs.act, sa, sb))
-        ysh = None if y_shared_host is None else y_shared_host[t:t + 1]
+            if route_dst[t, j] >= 0:
+                uses.setdefault(int(ids[t, j]), []).append((i, j))
+    y = np.zeros((len(tokens), cs.k, cs.H))
+
+    def run(e):
+        a, b, sa, sb = host_expert(inp_dev, e)
+        rows = [tokens[i] for i, _ in uses[e]]
+        return e, oracle.expert_rows(x_host[rows], a, b, cs.act, sa, sb)
+
+    for e, ye in parallel_map(run, sorted(uses)):
+        for n, (i, j) in enumerate(uses[e]):
+            y[i, j] = ye[n]
+    out = np.zeros((len(tokens), cs.H))
+    for i, t in enumerate(tokens):
         rd = route_dst[t:t + 1]
-        yy = np.concatenate(y_rows, 0)
         # combine with the routed rows renumbered 0..k-1 for this token
         local = np.where(rd >= 0, np.arange(cs.k)[None, :], rd).astype(np.int32)
-        acc_rows = oracle.combine(local, w[t:t + 1], yy, ysh)
-        ys.append(acc_rows[0])
-    return np.stack(ys) if ys else np.zeros((0, cs.H))
+        ysh = None if y_shared_host is None else y_shared_host[i:i + 1]
+        out[i] = oracle.combine(local, w[t:t + 1], y[i], ysh)[0]
+    return out
 
 
 def oracle_shared(cs, inp_host, tokens):
