@@ -237,6 +237,26 @@ moe_status moe_forward(const moe_problem *p, const void *x, const float *logits,
                        void *out, const moe_meta *meta, void *ws,
                        size_t ws_bytes, void *stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and results without `ws` / `ws_bytes`.  Its workspace is
+ * a device array inside the library, MOE_STATIC_SCRATCH_BYTES bytes on every
+ * GPU it runs on, held until the process ends.  A problem whose
+ * moe_workspace_bytes() exceeds that returns MOE_ERR_WORKSPACE before
+ * anything is enqueued (the decode and ReLU-square shapes and prefill
+ * batches of a few hundred tokens fit).  It calls no allocating routine.
+ * The first call on a device also enqueues, on `stream`, a clear of the
+ * array's control words.  All calls on one GPU share its array: calls that
+ * may overlap on one GPU (different streams, or threads) race and must be
+ * ordered by the caller.  Malformed routes still poison their tokens' rows;
+ * their count is kept in the array and not reported. */
+#define MOE_STATIC_SCRATCH_BYTES (32u << 20)
+moe_status moe_forward_static(const moe_problem *p, const void *x, const float *logits,
+                              const float *score_bias, const int32_t *ids_in, const float *w_in,
+                              const void *w13, const void *w2, const float *s13,
+                              const float *s2, const void *w13_sh, const void *w2_sh,
+                              void *out, const moe_meta *meta, void *stream);
+
 /* Synchronise `stream`, return the number of malformed routes seen since
  * the last call in *n_invalid_routes, and clear the counter. */
 moe_status moe_error(void *ws, size_t ws_bytes, void *stream,

@@ -23,8 +23,9 @@ MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 
 # every symbol the header declares
 EXPORTS = ("moe_workspace_bytes", "moe_workspace_init", "moe_route", "moe_dispatch",
-           "moe_expert_ffn", "moe_shared_ffn", "moe_combine", "moe_forward", "moe_error",
-           "moe_status_string")
+           "moe_expert_ffn", "moe_shared_ffn", "moe_combine", "moe_forward", "moe_forward_static",
+           "moe_error", "moe_status_string")
+MOE_STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class moe_problem(C.Structure):
@@ -71,6 +72,7 @@ def lib() -> C.CDLL:
             "moe_shared_ffn": [pp, P, P, P, P, P, S, P],
             "moe_combine": [pp, P, P, P, P, P, P, S, P],
             "moe_forward": [pp, P, P, P, P, P, P, P, P, P, P, P, P, C.POINTER(moe_meta), P, S, P],
+            "moe_forward_static": [pp, P, P, P, P, P, P, P, P, P, P, P, P, C.POINTER(moe_meta), P],
             "moe_error": [P, S, P, C.POINTER(i32)],
         }
         for name, args in sig.items():
@@ -160,25 +162,44 @@ def moe_combine(p, y_disp, route_dst, w, y_shared, out, ws, stream=None):
                                             _stream(stream)))
 
 
+def _meta(meta):
+    """moe_meta from a dict (see moe_forward); the event array is returned
+    too, to be kept alive across the call."""
+    if not meta:
+        return None, None
+    vals = [_p(meta.get(n)) for n, _ in moe_meta._fields_[:6]]
+    evs = meta.get("stage_events")
+    keep = None
+    if evs is not None:
+        assert len(evs) == MOE_N_STAGES
+        keep = (C.c_void_p * MOE_N_STAGES)(*[None if e is None else e.cuda_event for e in evs])
+    return moe_meta(*vals, C.cast(keep, C.c_void_p) if keep is not None else None), keep
+
+
 def moe_forward(p, x, logits, score_bias, ids_in, w_in, w13, w2, s13, s2, w13_sh, w2_sh, out,
                 meta, ws, stream=None):
     """`meta` is None or a dict with any of ids, w, counts, offsets, row_src,
     route_dst (device tensors receiving the metadata) and stage_events (a
     list of MOE_N_STAGES torch.cuda.Event or None)."""
-    m = None
-    keep = None
-    if meta:
-        vals = [_p(meta.get(n)) for n, _ in moe_meta._fields_[:6]]
-        evs = meta.get("stage_events")
-        if evs is not None:
-            assert len(evs) == MOE_N_STAGES
-            keep = (C.c_void_p * MOE_N_STAGES)(*[None if e is None else e.cuda_event for e in evs])
-        m = moe_meta(*vals, C.cast(keep, C.c_void_p) if keep is not None else None)
+    m, keep = _meta(meta)
     _check("moe_forward", lib().moe_forward(
         C.byref(p), _p(x), _p(logits), _p(score_bias), _p(ids_in), _p(w_in), _p(w13), _p(w2),
         _p(s13), _p(s2),
         _p(w13_sh), _p(w2_sh), _p(out), C.byref(m) if m is not None else None, _p(ws),
         ws.numel(), _stream(stream)))
+    del keep
+
+
+def moe_forward_static(p, x, logits, score_bias, ids_in, w_in, w13, w2, s13, s2, w13_sh, w2_sh,
+                       out, meta, stream=None):
+    """moe_forward without a workspace argument: the library's own
+    per-device array of MOE_STATIC_SCRATCH_BYTES serves as workspace."""
+    m, keep = _meta(meta)
+    _check("moe_forward_static", lib().moe_forward_static(
+        C.byref(p), _p(x), _p(logits), _p(score_bias), _p(ids_in), _p(w_in), _p(w13), _p(w2),
+        _p(s13), _p(s2), _p(w13_sh), _p(w2_sh), _p(out), C.byref(m) if m is not None else None,
+        _stream(stream)))
+    del keep
 
 
 def moe_error(ws, stream=None) -> int:

@@ -11,6 +11,7 @@
 #include <climits>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 
@@ -684,6 +685,61 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
     if (P.T > 0) e = launch_combine(ybuf, 0, route_dst, nullptr, y_sh, out, P.T, P.k, P.H, P.act_dtype, s);
     if (e == hipSuccess) e = mark(m, MOE_STAGE_COMBINE, s);
     return hip_status(e);
+}
+
+}  // extern "C"
+
+// ---- moe_forward_static: the layer without a caller workspace ---------------
+// Its workspace is a file-scope device array (one copy per GPU, alive until
+// the process ends).  In host code `scratch` only names the symbol: its
+// device address is looked up once per device with hipGetSymbolAddress and
+// that address is what the kernels get.
+namespace rde {
+
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's array.  The first call on a device looks
+// it up and clears the control words (malformed-route counter, the count
+// kernel's arrival ticket) with a fill kernel on `s`, ahead of that call's
+// own kernels; the count kernel leaves its ticket at zero after every launch.
+moe_status static_scratch(hipStream_t s, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+        if (((uintptr_t)ptr & 255) != 0) return MOE_ERR_HIP;
+        if (launch_fill_i32((int32_t*)ptr, CTRL_WORDS, 0, s) != hipSuccess) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace rde
+
+extern "C" {
+
+moe_status moe_forward_static(const moe_problem* p, const void* x, const float* logits,
+                              const float* score_bias, const int32_t* ids_in, const float* w_in,
+                              const void* w13, const void* w2, const float* s13, const float* s2,
+                              const void* w13_sh, const void* w2_sh, void* out,
+                              const moe_meta* meta, void* stream) {
+    moe_status st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (layout_of(*p).total > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((st = static_scratch((hipStream_t)stream, &ws)) != MOE_OK) return st;
+    return moe_forward(p, x, logits, score_bias, ids_in, w_in, w13, w2, s13, s2, w13_sh, w2_sh, out,
+                       meta, ws, (size_t)MOE_STATIC_SCRATCH_BYTES, stream);
 }
 
 moe_status moe_error(void* ws, size_t ws_bytes, void* stream, int32_t* n_invalid_routes) {
