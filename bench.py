@@ -2,10 +2,14 @@
 
 A step is one moe_forward call (route -> count-first dispatch -> expert FFN
 -> combine) over one batch of synthetic, HBM-resident inputs.  The default
-workload is the prefill dispatch shape: T = 2048 tokens, hidden 2048, 128
-experts, top-8, capacity 2048, SwiGLU intermediate 1024, bf16 with float32
-accumulation, router logits N(0, 1).  The other token buckets (256, 8192)
-are timed as a short sweep.
+workload is the largest one-GPU shape, the skewed prefill: T = 8192 tokens,
+hidden 7168, 256 experts, top-8, capacity 512, SwiGLU intermediate 2048,
+bf16 with float32 accumulation, router logits N(0, 1) plus a Zipf(1.1)
+per-expert bias (some experts overflow their capacity, others stay empty).
+Every other workload shape is timed as a short sweep: the fp32 layer, the
+prefill token buckets 256 / 2048 / 8192, decode with shared experts at 1 / 8
+/ 32 tokens, the ReLU-square shapes at 1 / 8 / 16 rows (distinct and
+shared routes), sigmoid routing, and the skewed layer with e4m3 weights.
 
 Printed: one JSON line with tokens/s (whole job), us per layer, the stage
 breakdown from HIP events recorded by the library on its stream inside the
@@ -26,6 +30,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+F32_PEAK_TFLOPS = 157.3      # MI355X fp32 (the float32 layer's GEMMs run on the vector ALUs)
+DECODE_ROWS_PER_EXPERT = 12  # the library's switch to the slot-indexed decode GEMMs
+FUSE_MAX_T, FUSE_MAX_Q, FUSE_MAX_E = 8, 256, 256   # routing inside the gate/up decode launch
+ORACLE_FLOPS = 4.6e8         # the oracle's rate on one core (double, widening per element)
+CPU_SAMPLE_S = 20.0          # target length of the CPU oracle sample
 N_BANKS = 4                  # rotating x / logits banks
 MIN_WARMUP_S = 0.2           # shortest warm-up of a sweep workload
 SWEEP_MIN_TIMED_S = 0.02     # shortest plain timed region of a sweep workload
@@ -36,10 +45,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--workload", default="prefill_T2048")
-    ap.add_argument("--sweep", default="prefill_T256,prefill_T8192,decode_T1,decode_T8,"
-                    "decode_T32,relu2_distinct_R16,relu2_shared_R1,sigmoid_T2048,skewed_bf16,"
-                    "skewed_fp8",
+    ap.add_argument("--workload", default="skewed_bf16")
+    ap.add_argument("--sweep", default="tiny_fp32,prefill_T256,prefill_T2048,prefill_T8192,"
+                    "decode_T1,decode_T8,decode_T32,relu2_distinct_R1,relu2_shared_R1,"
+                    "relu2_distinct_R8,relu2_shared_R8,relu2_distinct_R16,relu2_shared_R16,"
+                    "sigmoid_T2048,skewed_fp8",
                     help="comma-separated extra workloads timed briefly ('' = none)")
     ap.add_argument("--dispatch", default="prefill_T2048,prefill_T8192,skewed_bf16",
                     help="comma-separated workloads whose moe_route / moe_dispatch (with the "
@@ -52,8 +62,9 @@ def parse():
                     help="run one device copy of this size first (counter calibration)")
     ap.add_argument("--protocols", type=int, default=1,
                     help="1: also time cold calls (median/p95) and a captured graph of calls")
-    ap.add_argument("--cpu-tokens", type=int, default=128,
-                    help="tokens of the CPU oracle sample (0 = skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=-1,
+                    help="tokens of the CPU oracle sample (0 = skip, -1 = sized to about "
+                         "20 s of oracle work)")
     return ap.parse_args()
 
 
@@ -79,9 +90,39 @@ def stage_bytes_flops(cs, R, touched, ab, wb):
     }
     if cs.n_shared:
         Is, S = cs.I_shared, cs.n_shared
-        st["shared"] = (S * 3 * Is * H * 2 + T * H * ab + T * H * 4 + 2 * T * S * Is * ab,
-                        S * 2 * T * H * 3 * Is)
+        sh1 = (S * 2 * Is * H * 2 + T * H * ab + T * S * Is * ab, S * 2 * T * H * 2 * Is)
+        sh2 = (S * Is * H * 2 + T * S * Is * ab + T * H * 4, S * 2 * T * H * Is)
+        if decode_mode(cs):
+            # the decode launches stream the shared experts' weights too: their
+            # gate/up in the gate/up launch, their down projection in the other
+            st["gemm1"] = tuple(a + b for a, b in zip(st["gemm1"], sh1))
+            st["gemm2"] = tuple(a + b for a, b in zip(st["gemm2"], sh2))
+        else:
+            st["shared"] = tuple(a + b for a, b in zip(sh1, sh2))
+    if fused_mode(cs):
+        # routing and dispatch run inside the gate/up launch
+        moved = [st.pop(k) for k in ("route", "count", "scatter")]
+        st["gemm1"] = (st["gemm1"][0] + sum(m[0] for m in moved), st["gemm1"][1])
+        st.update(route=(0, 0), count=(0, 0), scatter=(0, 0))
     return st
+
+
+def decode_mode(cs):
+    """The library runs the slot-indexed decode GEMMs (bf16 layers with at most
+    12 routes per expert on average)."""
+    return cs.act_fmt != 0 and cs.T * cs.k <= DECODE_ROWS_PER_EXPERT * cs.E
+
+
+def fused_mode(cs):
+    """The gate/up decode launch also routes and dispatches the batch."""
+    return (decode_mode(cs) and 0 < cs.T <= FUSE_MAX_T and cs.T * cs.k <= FUSE_MAX_Q
+            and cs.E <= FUSE_MAX_E and cs.w_fmt == 1)
+
+
+def flops_peak_tflops(cs):
+    """Matrix peak of the layer's GEMM arithmetic: bf16 MFMA (e4m3 weights are
+    widened to bf16 in registers), or the fp32 vector peak for float32 layers."""
+    return F32_PEAK_TFLOPS if cs.act_fmt == 0 else BF16_PEAK_TFLOPS
 
 
 def run_workload(name, steps, warmup, with_events=True, protocols=False, min_warmup_s=0.0,
@@ -133,6 +174,7 @@ def run_workload(name, steps, warmup, with_events=True, protocols=False, min_war
         if i % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    n_warm = i
     # timed region 1: plain steps (the throughput figure), at least
     # min_timed_s of them at the warm-up's rate, so that the synchronisations
     # bracketing the region stay small against it
@@ -170,7 +212,8 @@ def run_workload(name, steps, warmup, with_events=True, protocols=False, min_war
     touched = sum(1 for e in range(cs.E) if off[e + 1] > off[e])
     ab = 4 if cs.act_fmt == synth.FMT_F32 else 2
     wb = {synth.FMT_F32: 4, synth.FMT_BF16: 2, synth.FMT_E4M3: 1}[cs.w_fmt]
-    return dict(cs=cs, steps=steps, n_plain=n_plain, wall=wall, wall_ev=wall_ev, stages=stages, R=R,
+    return dict(cs=cs, steps=steps, n_plain=n_plain, n_warm=n_warm, wall=wall, wall_ev=wall_ev,
+                stages=stages, R=R,
                 touched=touched, bf=stage_bytes_flops(cs, R, touched, ab, wb), base=base,
                 protocols=proto, graph_us=graph_us)
 
@@ -404,12 +447,13 @@ def dominant_gemm(res):
 def roofline_of(res, stage):
     us = res["stages"][stage]
     byts, flops = res["bf"][stage]
+    fpk = flops_peak_tflops(res["cs"])
     t_hbm = byts / (HBM_PEAK_GBPS * 1e9)
-    t_mfma = flops / (BF16_PEAK_TFLOPS * 1e12)
+    t_mfma = flops / (fpk * 1e12)
     if t_mfma > t_hbm:
         ach = flops / (us * 1e-6) / 1e12
-        return {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+        return {"bound": "mfma" if fpk == BF16_PEAK_TFLOPS else "alu", "achieved": round(ach, 1),
+                "peak": fpk, "unit": "TFLOP/s", "frac": round(ach / fpk, 4),
                 "traffic": counted_traffic(res["cs"].name, stage),
                 "kernel": stage, "us": round(us, 2), "alg_flops": flops, "alg_bytes": byts}
     ach = byts / (us * 1e-6) / 1e9
@@ -439,20 +483,23 @@ def layer_work(cs, R, touched):
     return byts, flops
 
 
-def layer_roofline(res, copy_gbps=None):
+def layer_roofline(res, ceiling_gbps=None):
     """t_roofline / t_measured for the whole layer, t_roofline = max(bytes /
-    HBM peak, flops / bf16 MFMA peak); `frac_copy` takes the measured device
-    copy bandwidth in place of the HBM peak."""
+    HBM peak, flops / matrix peak); `frac_measured` takes the measured HBM
+    ceiling of the same run (the faster of a device copy and a read stream)
+    in place of the HBM peak."""
     byts, flops = layer_work(res["cs"], res["R"], res["touched"])
+    fpk = flops_peak_tflops(res["cs"])
     t_meas = res["wall"] / res.get("n_plain", res["steps"])
-    t_h, t_m = byts / (HBM_PEAK_GBPS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
+    t_h, t_m = byts / (HBM_PEAK_GBPS * 1e9), flops / (fpk * 1e12)
     out = {"alg_bytes": byts, "alg_flops": flops, "t_hbm_us": round(t_h * 1e6, 2),
-           "t_mfma_us": round(t_m * 1e6, 2), "bound": "mfma" if t_m > t_h else "hbm",
+           "t_mfma_us": round(t_m * 1e6, 2),
+           "bound": ("mfma" if fpk == BF16_PEAK_TFLOPS else "alu") if t_m > t_h else "hbm",
            "t_roofline_us": round(max(t_h, t_m) * 1e6, 2),
            "frac": round(max(t_h, t_m) / t_meas, 4)}
-    if copy_gbps:
-        t_hc = byts / (copy_gbps * 1e9)
-        out["frac_copy"] = round(max(t_hc, t_m) / t_meas, 4)
+    if ceiling_gbps:
+        t_hc = byts / (ceiling_gbps * 1e9)
+        out["frac_measured"] = round(max(t_hc, t_m) / t_meas, 4)
     return out
 
 
@@ -474,7 +521,28 @@ def measure_copy_gbps(torch, mib=1024, reps=5):
     return round(2 * n / sec / 1e9, 1)
 
 
-def summary(res, copy_gbps=None):
+def measure_read_gbps(torch, mib=2048, reps=5):
+    """A read stream: row sums of a `mib` MiB float32 tensor of 4096-float
+    rows (every byte read once per call; one float written per 16 KiB row):
+    bytes read per second.  Of the torch reductions and products tried on
+    MI355X this one streams fastest (a whole-tensor sum is slower than a
+    device copy)."""
+    n = (mib << 20) // 4
+    src = torch.ones((n // 4096, 4096), dtype=torch.float32, device="cuda:0")
+    for _ in range(2):
+        src.sum(dim=1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        src.sum(dim=1)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del src
+    return round(4 * n / sec / 1e9, 1)
+
+
+def summary(res, ceiling_gbps=None):
     cs, st, bf = res["cs"], res["stages"], res["bf"]
     disp_us = st["count"] + st["scatter"]
     disp_b = bf["count"][0] + bf["scatter"][0]
@@ -485,33 +553,61 @@ def summary(res, copy_gbps=None):
         "sum_of_stage_us": round(sum(st.values()), 2),
         "dispatch_us": round(disp_us, 2),
         "dispatch_bytes": disp_b,
-        "gemm_mfma_pct": round(100 * g_fl / (g_us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 2),
+        "gemm_mfma_pct": round(100 * g_fl / (g_us * 1e-6) / (flops_peak_tflops(cs) * 1e12), 2),
         "gemm_hbm_GBps": round((bf["gemm1"][0] + bf["gemm2"][0]) / (g_us * 1e-6) / 1e9, 1),
         "kept_rows": res["R"], "experts_touched": res["touched"],
         "stages_us": {k: round(v, 2) for k, v in st.items()},
         "ms_per_step_with_stage_events": round(res["wall_ev"] / res["steps"] * 1e3, 4)
         if res.get("wall_ev") else None,
-        "layer_roofline": layer_roofline(res, copy_gbps),
+        "layer_roofline": layer_roofline(res, ceiling_gbps),
     }
+
+
+def cpu_sample_tokens(cs):
+    """Tokens of the CPU oracle sample: about CPU_SAMPLE_S seconds of oracle
+    work at its single-core rate (every route of the sample is assumed kept)."""
+    n_w = 2 * cs.I if cs.act == 0 else cs.I
+    per_token = cs.k * 2 * cs.H * (n_w + cs.I)
+    if cs.n_shared:
+        per_token += cs.n_shared * 2 * cs.H * 3 * cs.I_shared
+    return int(max(1, min(cs.T, round(CPU_SAMPLE_S * ORACLE_FLOPS / per_token))))
 
 
 def cpu_baseline(res, n_tokens):
     """The oracle as it stands, single-threaded, on the first n_tokens tokens
-    of the same workload (same weights, capacity and expert count)."""
+    of the same workload (same weights, capacity and expert count).  Only the
+    experts those tokens route to are copied to the host.  Besides the
+    sample's own rate, the whole layer is extrapolated from its time per kept
+    route (the full batch keeps res['R'] routes; on the skewed workload most
+    routes are dropped by capacity, which a short sample of early tokens does
+    not see)."""
+    import numpy as np
     import oracle
     import synth
 
     cs = res["cs"]
     sub = synth.replace(cs, T=n_tokens)
     base = res["base"]
-    x = oracle.from_torch(base.x[:n_tokens])
-    lg = oracle.from_torch(base.logits[:n_tokens])
-    w13 = oracle.from_torch(base.w13)
-    w2 = oracle.from_torch(base.w2)
     conv = lambda t: None if t is None else oracle.from_torch(t)
-    r = oracle.forward(sub, x, lg, w13, w2, conv(base.s13), conv(base.s2), conv(base.w13_sh),
-                       conv(base.w2_sh), score_bias=conv(base.score_bias))
+    x = conv(base.x[:n_tokens])
+    lg = conv(base.logits[:n_tokens])
+    bias = conv(base.score_bias)
+    ids, _ = oracle.route(lg, cs.k, cs.renormalize, cs.score_func, bias, cs.route_scale)
+    touched = sorted(set(ids.ravel().tolist()))
+
+    def host_weights(t):
+        if t is None:
+            return None
+        h = np.zeros(tuple(t.shape), dtype=conv(t[:1]).dtype)   # untouched experts stay zero pages
+        for e in touched:
+            h[e] = conv(t[e])
+        return h
+
+    w13, w2, s13, s2 = (host_weights(t) for t in (base.w13, base.w2, base.s13, base.s2))
+    r = oracle.forward(sub, x, lg, w13, w2, s13, s2, conv(base.w13_sh), conv(base.w2_sh),
+                       score_bias=bias)
     sec = r["seconds"]
+    kept = int(r["offsets"][-1])
     try:
         host_cores = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -522,11 +618,17 @@ def cpu_baseline(res, n_tokens):
             model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
     except OSError:
         pass
+    per_route = sec / max(kept, 1)
+    full_s = per_route * res["R"] if kept else sec / n_tokens * cs.T
     return {"value": round(n_tokens / sec, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "host_cores": host_cores, "cpu_model": model,
-            "sample": f"first {n_tokens} of {cs.T} tokens of {cs.name}: routing, count-first "
-                      f"dispatch, expert FFN and combine for them ({sec:.1f} s)",
-            "us_per_layer_extrapolated": round(sec / n_tokens * cs.T * 1e6, 1)}
+            "sample": f"first {n_tokens} of {cs.T} tokens of {cs.name} ({kept} kept routes): "
+                      f"routing, count-first dispatch, expert FFN and combine for them, "
+                      f"{sec:.1f} s on one core",
+            "us_per_kept_route": round(per_route * 1e6, 1),
+            "us_per_layer_extrapolated": round(full_s * 1e6, 1),
+            "tokens_per_s_extrapolated": round(cs.T / full_s, 3),
+            "extrapolation": f"time per kept route x the {res['R']} kept routes of the full batch"}
 
 
 def main():
@@ -547,17 +649,23 @@ def main():
         del src, dst
     print(f"[bench] workload {args.workload}: warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
-    res = run_workload(args.workload, args.steps, args.warmup, protocols=bool(args.protocols))
+    # at least MIN_WARMUP_S of warm-up steps (more than --warmup when those
+    # take less): the GPU reaches its steady clocks before the timed region
+    res = run_workload(args.workload, args.steps, args.warmup, protocols=bool(args.protocols),
+                       min_warmup_s=MIN_WARMUP_S)
     copy_gbps = measure_copy_gbps(torch) if args.protocols else None
+    read_gbps = measure_read_gbps(torch) if args.protocols else None
+    ceiling = max(copy_gbps, read_gbps) if args.protocols else None
     cs = res["cs"]
     ms = res["wall"] / res["n_plain"] * 1e3
-    summ = summary(res, copy_gbps)
+    summ = summary(res, ceiling)
     dom = dominant_gemm(res)
     line = {
         "metric": "MoE layer tokens/s + us/layer; dispatch HBM GB/s, grouped-GEMM MFMA % of peak",
         "value": round(cs.T / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "warmup_steps_run": res["n_warm"],
         "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cs.act_fmt == 1 else "f32",
@@ -569,6 +677,8 @@ def main():
         **summ,
         "roofline": roofline_of(res, dom),
         "copy_GBps": copy_gbps,
+        "read_GBps": read_gbps,
+        "hbm_ceiling_GBps": ceiling,
     }
     if res.get("protocols"):
         pr = dict(res["protocols"])
@@ -576,10 +686,10 @@ def main():
         line["protocols"] = pr
     print(f"[bench] {cs.name}: {ms*1e3:.1f} us/step, stages {summ['stages_us']}",
           file=sys.stderr, flush=True)
-    if args.cpu_tokens > 0:
-        print(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens", file=sys.stderr,
-              flush=True)
-        line["cpu_baseline"] = cpu_baseline(res, args.cpu_tokens)
+    n_cpu = cpu_sample_tokens(cs) if args.cpu_tokens < 0 else args.cpu_tokens
+    if n_cpu > 0:
+        print(f"[bench] cpu baseline: oracle on {n_cpu} tokens", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(res, n_cpu)
     del res["base"]
     sweep = {}
     for name in [s for s in args.sweep.split(",") if s]:
@@ -587,7 +697,7 @@ def main():
         r2 = run_workload(name, max(5, args.steps // 3), 10, min_warmup_s=MIN_WARMUP_S,
                           min_timed_s=SWEEP_MIN_TIMED_S, graph=True)
         ms2 = r2["wall"] / r2["n_plain"] * 1e3
-        sw = summary(r2, copy_gbps)
+        sw = summary(r2, ceiling)
         sw["tokens_per_s"] = round(r2["cs"].T / (ms2 * 1e-3), 1)
         sw["ms_per_step"] = round(ms2, 4)
         sw["steps"] = r2["n_plain"]
