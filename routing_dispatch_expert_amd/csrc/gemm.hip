@@ -17,13 +17,14 @@
 // never depends on the routing and no host synchronisation is needed.
 //
 // bf16 kernel: 512 threads = 8 waves, block tile BM x BN x BK =
-// 256 x 256 x 32, wave tile 128 x 64 = 4 x 2 MFMA v_mfma_f32_32x32x16_bf16
+// 256 x 256 x 64, wave tile 128 x 64 = 4 x 2 MFMA v_mfma_f32_32x32x16_bf16
 // blocks, one workgroup per CU.  Operands go straight from global memory to
-// a 4-stage LDS ring (global_load_lds_dwordx4), three k-tiles in flight
-// while one is multiplied, one barrier per k-tile; rows of 64 bytes with an
-// XOR chunk swizzle keep the fragment reads free of bank conflicts.  The ring
-// runs on across the tiles of a workgroup (the next tile's first k-tiles load
-// during the current tile's last ones).  Rows of a tile past the end of its
+// a 2-stage LDS ring of 64 KB stages (global_load_lds_dwordx4): each operand
+// row of a k-tile is one whole 128-byte line, requested once, and one
+// k-tile (64 KB) is in flight while the other is multiplied, one barrier
+// per k-tile; an XOR chunk swizzle keeps the fragment reads free of bank
+// conflicts.  The ring runs on across the tiles of a workgroup (the next
+// tile's first k-tile loads during the current tile's last one).  Rows of a tile past the end of its
 // expert cost neither loads (16-row groups) nor MFMAs (32-row blocks).  bf16
 // results are regrouped in a small per-wave LDS patch so that stores write
 // 64 contiguous bytes per row.
@@ -87,12 +88,20 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // e4m3 k-tiles are 64 wide: a B row is 64 e4m3 bytes in the same swizzled
 // 64-byte layout, and A holds two such 64-byte halves (k 0..31, k 32..63)
 // one after the other.
-constexpr int kStages = 4;
 constexpr int A_STAGE = BM * BK * 2;          // bytes of one 64-byte-row A half (16 KB)
 constexpr int B_STAGE = BN * 64;              // 256 rows x 64 B (16 KB)
+constexpr int W_STAGE = BM * 128;             // bf16: 256 rows x 128 B (one operand, 32 KB)
 constexpr int kOutPitch = 80;                 // bytes per row of a wave's 32 x 32 bf16 output patch
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 1 | (((r >> 2) & 1) << 1); }
+// 128-byte rows (bf16 k-tiles): chunk c of row r at slot c ^ swz8(r).  8
+// consecutive rows reading one logical chunk hit 8 distinct slots, and 16
+// consecutive rows hit 16 distinct 16-byte positions of a 256-byte bank
+// window (rows r and r + 8 differ in bit 0 of the slot, and odd rows start
+// 128 bytes in), so the fragment reads are free of bank conflicts whether
+// the LDS serves 8 or 16 lanes of a ds_read_b128 per clock.  swz8 depends on
+// bits 0..3 of the row only.
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // LDS byte address of a __shared__ object (32-bit, as the hardware sees it).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -181,19 +190,24 @@ __device__ __forceinline__ void wait_barrier_dyn(int n) {
 template <int EPI, bool FP8, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int NT = NW * 64;                  // threads
-    constexpr int BKT = FP8 ? 64 : BK;           // k per k-tile: 64-byte weight-row pieces
-    constexpr int AM = BKT / BK;                 // 64-byte A halves per k-tile
-    constexpr int STG = FP8 ? 3 : kStages;       // ring stages (3 x 48 KB or 4 x 32 KB)
-    constexpr int A_ST = AM * A_STAGE;           // bytes of one A stage
+    constexpr bool WIDE = !FP8;                  // bf16: 128-byte operand rows (64 k per k-tile)
+    constexpr int BKT = 64;                      // k per k-tile
+    constexpr int AM = WIDE ? 1 : BKT / BK;      // A pieces per k-tile (e4m3: two 64-byte halves)
+    constexpr int STG = FP8 ? 3 : 2;             // ring stages (3 x 48 KB or 2 x 64 KB)
+    constexpr int A_ST = WIDE ? W_STAGE : AM * A_STAGE;   // bytes of one A stage
+    constexpr int B_ST = WIDE ? W_STAGE : B_STAGE;        // bytes of one B stage
+    constexpr int RB = WIDE ? 128 : 64;          // LDS bytes per operand row
+    constexpr int DR = 1024 / RB;                // rows per DMA instruction: 8 or 16
     constexpr int WB = FP8 ? 1 : 2;              // weight bytes per element
     constexpr bool OUT_IN_RING = FP8;            // epilogue patch in the ring slot just used
     constexpr int BW = BN / (NW / 2);            // B rows (wave tile columns) per wave: 64 or 128
     constexpr int NBW = BW / 32;                 // 32-column MFMA blocks per wave: 2 or 4
-    constexpr int LB = 16 / NW;                  // B DMA instructions per thread per k-tile
-    constexpr int GA = 16 / NW;                  // A 16-row groups per wave: 2 or 4
+    constexpr int LB = BN / DR / NW;             // B DMA instructions per thread per k-tile
+    constexpr int GA = BM / DR / NW;             // A row groups (DR rows) per wave: 2 or 4
     static_assert(!OUT_IN_RING || NW * 32 * kOutPitch <= A_ST, "output patch fits in an A stage");
+    static_assert(!WIDE || NW == 8, "the 128-byte-row plan is laid out for 8 waves");
     __shared__ __attribute__((aligned(1024))) unsigned char sA[STG][A_ST];
-    __shared__ __attribute__((aligned(1024))) unsigned char sB[STG][B_STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char sB[STG][B_ST];
     __shared__ int32_t s_mt[kMaxGroupsLds + 1], s_off[kMaxGroupsLds + 1];
     __shared__ __attribute__((aligned(16))) unsigned char sOut[OUT_IN_RING ? 1 : NW][OUT_IN_RING ? 16 : 32 * kOutPitch];
     // EPI_COMBINE: the tile's routes and their weights, loaded during the
@@ -233,13 +247,15 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     // ring slot of a running k-tile count
     auto ring = [](int x) { return (STG & (STG - 1)) == 0 ? (x & (STG - 1)) : (x % STG); };
 
-    // DMA plan.  A: wave w fills the 16-row groups w + NW*i (row 16*group +
-    // lane/4), i < GA; with 8 waves a group wholly past the expert's last row
-    // is not loaded, so a half-filled tile issues half the A traffic and
-    // every wave still has one A group while rows > 128; a 64-wide k-tile
-    // loads each group twice (both halves).  B: wave w fills rows
-    // w*16*LB + 16*b + lane/4 (b < LB), 64 bytes per row (32 bf16 or 64 e4m3).
-    const int dr = lane >> 2, ds = lane & 3;
+    // DMA plan.  A: wave w fills the DR-row groups w + NW*i (row DR*group +
+    // lane/(RB/16)), i < GA; with 8 waves a group wholly past the expert's
+    // last row is not loaded, so a half-filled tile issues half the A traffic
+    // and every wave keeps A groups while rows > 128; e4m3 k-tiles load each
+    // 16-row group twice (both 64-byte halves).  B: wave w fills rows
+    // w*DR*LB + DR*b + lane/(RB/16) (b < LB): 128 bytes per row (64 bf16), or
+    // 64 (64 e4m3).
+    const int dr = WIDE ? (lane >> 3) : (lane >> 2), ds = WIDE ? (lane & 7) : (lane & 3);
+    auto swzr = [](int r) { return WIDE ? swz8(r) : swz(r); };
 
     // wave-uniform LDS bases of this wave's DMA blocks in ring slot 0
     const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(sA[0]) + wave * 1024);
@@ -248,15 +264,23 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     // routes of the epilogue staged in LDS: needs k-tiles 1, 5 and 9 (see the k-loop)
     const bool route_pf = EPI == EPI_COMBINE && nk >= 10;
     const uint32_t lb0 = __builtin_amdgcn_readfirstlane(lds_addr(sB[0]) + wave * LB * 1024);
+    static_assert(!WIDE || GA * NW * DR == BM, "A row groups cover the tile");
 
     // A tile's place in the problem and this thread's DMA sources (byte
     // offsets at k = 0).  la = A groups this wave loads (0 .. GA).
+    // bf16 (128-byte rows): only the A row indices and the B row base depend on
+    // the tile; the chunk offsets depend on the lane alone (every A group of a
+    // wave shares one swizzle, and B rows alternate between two), and a wave's
+    // B rows are consecutive weight rows, so instruction b adds 8 b rows.
     struct Tile {
-        int g, nt, a_row0, rows, rot, la;
-        int64_t ga[GA];
+        int g, nt, a_row0, rows, rot, la, lbv;
+        int64_t ga[WIDE ? 1 : GA];
+        int32_t ar[WIDE ? GA : 1];
         int64_t gbase;          // the expert's weights (wave-uniform)
-        uint32_t gb[LB];        // per-lane weight offsets within them
+        uint32_t gb[WIDE ? 1 : LB];   // per-lane weight offsets within them (bf16: row base)
     };
+    const uint32_t a_chunk = (uint32_t)(ds ^ swz8(8 * wave + dr)) * 16;
+    const uint32_t b_chunk = (uint32_t)(ds ^ swz8(32 * wave + dr)) * 16;
     auto make_tile = [&](int64_t Lt) {
         Tile t;
         int cnt, ml;
@@ -302,7 +326,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
         // before any is used (one wait for the lookups)
         int64_t ar[GA];
 #pragma unroll
-        for (int i = 0; i < GA; ++i) ar[i] = t.a_row0 + min((wave + NW * i) * 16 + dr, rows - 1);
+        for (int i = 0; i < GA; ++i) ar[i] = t.a_row0 + min((wave + NW * i) * DR + dr, rows - 1);
         if (a.gather) {
             int32_t q[GA];
 #pragma unroll
@@ -310,16 +334,26 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
             for (int i = 0; i < GA; ++i) ar[i] = q[i] / a.k_top;
         }
-#pragma unroll
-        for (int i = 0; i < GA; ++i) {
-            const int ra = (wave + NW * i) * 16 + dr;
-            t.ga[i] = ar[i] * a.lda * 2 + ((ds ^ swz(ra)) * 16);
-        }
         t.gbase = (int64_t)g * a.b_group_stride * WB;
+        if (WIDE) {
 #pragma unroll
-        for (int b = 0; b < LB; ++b) {
-            const int rb = wave * 16 * LB + 16 * b + dr;
-            t.gb[b] = (uint32_t)brow_of(rb) * (uint32_t)a.k_seg * WB + ((ds ^ swz(rb)) * 16);
+            for (int i = 0; i < GA; ++i) t.ar[i] = (int32_t)ar[i];
+            // B rows wave*32 .. +31 (every one of them past N_w in a wave that
+            // loads none: N_w is a multiple of 128)
+            t.gb[0] = (uint32_t)brow_of(wave * 32 + dr) * (uint32_t)a.k_seg * WB;
+            t.lbv = EPI == EPI_SWIGLU || nt * BN + wave * 32 < a.N_w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < GA; ++i) {
+                const int ra = (wave + NW * i) * DR + dr;
+                t.ga[i] = ar[i] * a.lda * 2 + ((ds ^ swzr(ra)) * 16);
+            }
+#pragma unroll
+            for (int b = 0; b < LB; ++b) {
+                const int rb = wave * DR * LB + DR * b + dr;
+                t.gb[b] = (uint32_t)brow_of(rb) * (uint32_t)a.k_seg * WB + ((ds ^ swzr(rb)) * 16);
+            }
+            t.lbv = 1;
         }
         // K order: the tile starts at k-tile `rot` and wraps.  Tiles of
         // different experts running at the same time then read different
@@ -330,7 +364,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
         // fetched into L2 once and reused.  rot depends only on the expert, so
         // a row's summation order never depends on the other tokens.
         t.rot = (g * 13) % nk;
-        t.la = NW == 8 ? __builtin_amdgcn_readfirstlane((16 * wave < rows) + (16 * (wave + 8) < rows)) : GA;
+        if (WIDE) {
+            int la = 0;
+#pragma unroll
+            for (int i = 0; i < GA; ++i) la += DR * (wave + NW * i) < rows;
+            t.la = __builtin_amdgcn_readfirstlane(la);
+        } else {
+            t.la = NW == 8 ? __builtin_amdgcn_readfirstlane((16 * wave < rows) + (16 * (wave + 8) < rows)) : GA;
+        }
         return t;
     };
     // Load k-tile s (in the tile's own K order) of tile t into ring slot `slot`.
@@ -340,7 +381,20 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
         const int k0 = kr * BKT;
         const int seg = k0 / a.k_seg;
         const int64_t bo = (int64_t)seg * a.b_seg_stride + (k0 - seg * a.k_seg);
-        const uint32_t la = la0 + slot * A_ST, lb = lb0 + slot * B_STAGE;
+        const uint32_t la = la0 + slot * A_ST, lb = lb0 + slot * B_ST;
+        if (WIDE) {
+#pragma unroll
+            for (int i = 0; i < GA; ++i)
+                if (t.la > i) dma16(Ab + (int64_t)t.ar[i] * a.lda * 2 + a_chunk + (int64_t)k0 * 2, la + i * NW * 1024);
+            if (t.lbv) {
+                const char* bsrc = Bb + t.gbase + bo * WB;
+                const uint32_t bstep = 8u * (uint32_t)a.k_seg * WB;   // 8 weight rows
+#pragma unroll
+                for (int b = 0; b < LB; ++b)
+                    dma16(bsrc + (t.gb[0] + b * bstep + ((b & 1) ? (b_chunk ^ 16u) : b_chunk)), lb + b * 1024);
+            }
+            return;
+        }
 #pragma unroll
         for (int h = 0; h < AM; ++h)
 #pragma unroll
@@ -350,7 +404,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
         for (int b = 0; b < LB; ++b) dma16(Bb + t.gbase + t.gb[b] + bo * WB, lb + b * 1024);
     };
 
-    // The load ring runs across tiles: while a tile's last kStages - 1
+    // The load ring runs across tiles: while a tile's last STG - 1
     // k-tiles are multiplied, the next tile's first ones are loaded, so the
     // pipeline never drains between tiles.  Ring slot of k-tile s of a tile =
     // (sbase + s) % STG, sbase = k-tiles of this workgroup's earlier tiles (mod STG).
@@ -371,6 +425,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     // of them, and the blocks differ by compile-time constants.
     const int zr = swz(rA);
     const int loff0 = rA * 64 + ((half ^ zr) * 16), loff1 = rA * 64 + (((2 + half) ^ zr) * 16);
+    // 128-byte rows: step ks reads logical chunk 2 ks + half; swz8 depends on
+    // bits 0..3 of the row, so the row blocks share these four offsets too
+    int loffw[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) loffw[ks] = rA * 128 + (((2 * ks + half) ^ swz8(rA)) * 16);
     for (; Lt < total; Lt += G) {
         const bool has_next = Lt + G < total;
         const Tile nxt = has_next ? make_tile(Lt + G) : cur;
@@ -400,7 +459,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
             for (int kt = 0; kt < nk; ++kt) {
                 // in flight behind k-tile kt: k-tiles kt + 1 .. kt + STG - 2, of
                 // this tile or (at the end) of the next one
-                if (STG == 4) {
+                if (STG == 2) {
+                    // nothing is issued after k-tile kt before this wait
+                    waitcnt_barrier<0>();
+                } else if (STG == 4) {
                     if (kt + 2 < nk) waitcnt_barrier<2 * LC>();
                     else if (kt + 2 == nk) wait_barrier_dyn(LC + cn);
                     else wait_barrier_dyn(2 * cn);
@@ -431,8 +493,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
                     // this lane's k = 16 ks + 8 half .. + 7: logical 16-byte chunk c
                     // of the 64-byte A half ks / 2 and of a bf16 B row; in an e4m3
                     // B row, the 8-byte piece `half` of chunk ks
-                    const int lo = (ks & 1) ? loff1 : loff0;   // chunk c = 2 (ks & 1) + half
-                    const unsigned char* sa = sA[slot] + (ks >> 1) * A_STAGE;
+                    const int lo = WIDE ? loffw[ks] : ((ks & 1) ? loff1 : loff0);   // chunk c = 2 (ks & 1) + half
+                    const unsigned char* sa = sA[slot] + (WIDE ? 0 : (ks >> 1) * A_STAGE);
                     bf16x8 bv[NBW], av[NA > 0 ? NA : 1];
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb) {
@@ -440,12 +502,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
                         if (FP8) {
                             bv[nb] = e4m3x8_to_bf16x8(*(const uint2*)(sb + (r0 + rA) * 64 + ((ks ^ zr) * 16) + half * 8));
                         } else {
-                            bv[nb] = *(const bf16x8*)(sb + r0 * 64 + lo);
+                            bv[nb] = *(const bf16x8*)(sb + r0 * RB + lo);
                         }
                     }
 #pragma unroll
                     for (int mb = 0; mb < NA; ++mb) {
-                        av[mb] = *(const bf16x8*)(sa + (wm + 2 * mb) * 32 * 64 + lo);
+                        av[mb] = *(const bf16x8*)(sa + (wm + 2 * mb) * 32 * RB + lo);
                     }
 #pragma unroll
                     for (int mb = 0; mb < NA; ++mb)
@@ -456,7 +518,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
             }
         };
         auto by_la = [&](auto na_c) {
-            if (NW != 8) kloop(na_c, std::integral_constant<int, GA>{});   // every A group loaded
+            if (WIDE) kloop(na_c, std::integral_constant<int, 0>{});       // waits need no DMA count
+            else if (NW != 8) kloop(na_c, std::integral_constant<int, GA>{});   // every A group loaded
             else if (cur.la == 2) kloop(na_c, std::integral_constant<int, 2>{});
             else if (cur.la == 1) kloop(na_c, std::integral_constant<int, 1>{});
             else kloop(na_c, std::integral_constant<int, 0>{});
