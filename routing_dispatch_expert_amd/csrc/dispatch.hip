@@ -23,6 +23,7 @@
 // kept rows with 16-byte vector stores.  When no row copy is asked for, a
 // metadata-only variant takes one thread per route.
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "route_wave.h"
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
     int32_t* __restrict__ rexp, int32_t* __restrict__ lrank, int32_t* __restrict__ partial,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ mt_off,
     int32_t* __restrict__ ctrl, int32_t* __restrict__ route_dst, int32_t* __restrict__ row_src,
-    int64_t r_max) {
+    int64_t r_max, int delay) {
     extern __shared__ int32_t lds[];  // [kCountWaves][E] during counting; [2][E] in the scan
     __shared__ int s_last;
     __shared__ int32_t s_tot[2];
@@ -272,6 +273,11 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
     // later kernels.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    // `delay`: block 0 holds back its ticket (about 8k clocks per step), so
+    // that it arrives last and reads every other block's totals; a test of the
+    // hand-off sets it from the host (0 otherwise)
+    if (blockIdx.x == 0)
+        for (int i = 0; i < delay; ++i) __builtin_amdgcn_s_sleep(127);
     if (tid == 0)
         s_last = (__hip_atomic_fetch_add(&ctrl[CTRL_TICKET], 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1);
@@ -600,6 +606,12 @@ hipError_t launch_count_rank(const int32_t* ids, int T, int k, int E, int C, int
                              int32_t* lrank, int32_t* partial, int32_t* counts, int32_t* offsets,
                              int32_t* mt_off, int32_t* ctrl, hipStream_t s, int32_t* route_dst,
                              int32_t* row_src, int64_t r_max) {
+    // MOE_COUNT_DELAY (read once): hold back block 0's ticket by that many
+    // steps of about 8k clocks, so a test can make it the last block to arrive
+    static const int delay = [] {
+        const char* e = std::getenv("MOE_COUNT_DELAY");
+        return e ? std::atoi(e) : 0;
+    }();
     const int64_t Q = (int64_t)T * k;
     const int nb = count_blocks(Q) > 0 ? count_blocks(Q) : 1;
     int ebits = 1;
@@ -608,7 +620,7 @@ hipError_t launch_count_rank(const int32_t* ids, int T, int k, int E, int C, int
     if (route_dst != nullptr && nb != 1) return hipErrorInvalidValue;   // placement needs the one block
     hipLaunchKernelGGL(count_rank_kernel, dim3(nb), dim3(kWave * kCountWaves), lds, s, ids, Q, k, E,
                        ebits, C, bm, rexp, lrank, partial, counts, offsets, mt_off, ctrl, route_dst,
-                       row_src, r_max);
+                       row_src, r_max, delay);
     return hipGetLastError();
 }
 
