@@ -469,6 +469,15 @@ moe_status moe_dispatch(const moe_problem* p, const void* x, const int32_t* ids,
     if (p->T > 0 && (check_ptrs16({x, x_disp}) != MOE_OK || !ids || !row_src || !route_dst))
         return MOE_ERR_ARG;
     hipStream_t s = (hipStream_t)stream;
+    const int64_t Q = (int64_t)p->T * p->k;
+    if (Q > 0 && Q <= kPlaceMaxQ) {
+        // one workgroup counts, scans and places every route; then the copies
+        hipError_t e = launch_count_place(ids, p->T, p->k, p->E, p->C, gemm_bm(*p), counts, offsets,
+                                          at<int32_t>(ws, L.mt_off), row_src, r_max_of(*p), route_dst,
+                                          at<int32_t>(ws, L.ctrl), s);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        return hip_status(launch_copy_rows(x, p->T, p->H, p->k, act_bytes(*p), route_dst, x_disp, s));
+    }
     hipError_t e = launch_count_rank(ids, p->T, p->k, p->E, p->C, gemm_bm(*p), at<int32_t>(ws, L.rexp),
                                      at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), counts,
                                      offsets, at<int32_t>(ws, L.mt_off), at<int32_t>(ws, L.ctrl), s);
@@ -607,19 +616,29 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
                              route_scale_of(P), ids_out, w_out, s);
         if (e == hipSuccess) e = mark(m, MOE_STAGE_ROUTE, s);
         if (e != hipSuccess) return MOE_ERR_HIP;
-        // routes that fit one count block are placed by that block when no
-        // rows are copied: no separate scatter launch
-        const bool place = in_place && count_blocks(Q) <= 1;
-        e = launch_count_rank(ids, P.T, P.k, P.E, P.C, tile_bm, at<int32_t>(ws, L.rexp),
-                              at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), counts, offsets, mt,
-                              at<int32_t>(ws, L.ctrl), s, place ? route_dst : nullptr, row_src,
-                              r_max_of(P));
-        if (e == hipSuccess) e = mark(m, MOE_STAGE_COUNT, s);
-        if (e != hipSuccess) return MOE_ERR_HIP;
-        if (P.T > 0 && !place)
-            e = launch_scatter(x, P.T, P.H, P.k, P.E, P.C, act_bytes(P), r_max_of(P), at<int32_t>(ws, L.rexp),
-                               at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), offsets, route_dst,
-                               row_src, in_place ? nullptr : x_disp, s);
+        if (Q > 0 && Q <= kPlaceMaxQ) {
+            // one workgroup counts, scans and places every route (no hand-off
+            // between blocks); float32 layers then copy their rows
+            e = launch_count_place(ids, P.T, P.k, P.E, P.C, tile_bm, counts, offsets, mt, row_src,
+                                   r_max_of(P), route_dst, at<int32_t>(ws, L.ctrl), s);
+            if (e == hipSuccess) e = mark(m, MOE_STAGE_COUNT, s);
+            if (e == hipSuccess && !in_place)
+                e = launch_copy_rows(x, P.T, P.H, P.k, act_bytes(P), route_dst, x_disp, s);
+        } else {
+            // routes that fit one count block are placed by that block when no
+            // rows are copied: no separate scatter launch
+            const bool place = in_place && count_blocks(Q) <= 1;
+            e = launch_count_rank(ids, P.T, P.k, P.E, P.C, tile_bm, at<int32_t>(ws, L.rexp),
+                                  at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), counts, offsets, mt,
+                                  at<int32_t>(ws, L.ctrl), s, place ? route_dst : nullptr, row_src,
+                                  r_max_of(P));
+            if (e == hipSuccess) e = mark(m, MOE_STAGE_COUNT, s);
+            if (e == hipSuccess && P.T > 0 && !place)
+                e = launch_scatter(x, P.T, P.H, P.k, P.E, P.C, act_bytes(P), r_max_of(P),
+                                   at<int32_t>(ws, L.rexp), at<int32_t>(ws, L.lrank),
+                                   at<int32_t>(ws, L.partial), offsets, route_dst, row_src,
+                                   in_place ? nullptr : x_disp, s);
+        }
         if (e == hipSuccess) e = mark(m, MOE_STAGE_SCATTER, s);
         if (e != hipSuccess) return MOE_ERR_HIP;
     }

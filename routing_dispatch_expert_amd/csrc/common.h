@@ -70,6 +70,20 @@ hipError_t launch_count_rank(const int32_t* ids, int T, int k, int E, int C, int
                              int32_t* ctrl, hipStream_t s, int32_t* route_dst = nullptr,
                              int32_t* row_src = nullptr, int64_t r_max = 0);
 
+// At most kPlaceMaxQ routes: one 1024-thread workgroup ranks every route,
+// writes counts, offsets and the m-tile table, and places every route
+// (route_dst, row_src with -1 past the kept rows); no cross-block hand-off.
+// Above it the chain of 64-route ranking steps of one workgroup costs more
+// than the hand-off (measured: 16384 routes 34 against 21 us with the
+// multi-block kernel and its scatter launch; 2048 routes 13.6 against 18.5).
+constexpr int64_t kPlaceMaxQ = 4096;
+hipError_t launch_count_place(const int32_t* ids, int T, int k, int E, int C, int bm,
+                              int32_t* counts, int32_t* offsets, int32_t* mt_off, int32_t* row_src,
+                              int64_t r_max, int32_t* route_dst, int32_t* ctrl, hipStream_t s);
+// x -> x_disp copies of routes already placed (route_dst).
+hipError_t launch_copy_rows(const void* x, int T, int H, int k, int elem_bytes, const int32_t* route_dst,
+                            void* x_disp, hipStream_t s);
+
 // route_dst, row_src and the x -> x_disp row copies.
 hipError_t launch_scatter(const void* x, int T, int H, int k, int E, int C, int elem_bytes,
                           int64_t r_max, const int32_t* rexp, const int32_t* lrank,

@@ -565,6 +565,141 @@ __global__ __launch_bounds__(kSmallThreads) void small_dispatch_kernel(
     for (int64_t r = s_off[E] + tid; r < r_max; r += kSmallThreads) row_src[r] = -1;
 }
 
+// ---- one workgroup for the whole count-first dispatch of small batches ----
+// The multi-block count kernel pays three round trips through the device-
+// coherent level for its hand-off (write-through totals, the ticket, the
+// last block's reload).  Up to kPlaceMaxQ routes, one 1024-thread workgroup
+// instead ranks every route itself: wave w takes the contiguous routes
+// [64 PER w, 64 PER (w + 1)) in PER 64-route steps, ranks them by ballots
+// over the expert bits against its running LDS histogram (as count_rank
+// does), then the per-expert totals are prefix-summed over the 16 waves,
+// scanned into offsets and the m-tile table, and every route is placed
+// (route_dst, row_src) with no second launch.  A lane keeps each of its
+// routes as one packed word: (expert + 2) << 21 | in-wave rank.
+template <int PER>
+__global__ __launch_bounds__(kSmallThreads) void count_place_kernel(
+    const int32_t* __restrict__ ids, int Q, int k, int E, int ebits, int C, int bm,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ mt_off,
+    int32_t* __restrict__ row_src, int64_t r_max, int32_t* __restrict__ route_dst,
+    int32_t* __restrict__ ctrl) {
+    extern __shared__ int32_t lds[];   // hist [kSmallWaves][E], then offsets [E + 1]
+    __shared__ int32_t s_wsum[2][kSmallWaves], s_tot[2];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    int32_t* hist = lds;
+    int32_t* s_off = lds + kSmallWaves * E;
+    for (int i = tid; i < kSmallWaves * E; i += kSmallThreads) hist[i] = 0;
+    __syncthreads();
+    int32_t* wh = hist + wv * E;
+    const int q0 = wv * (kWave * PER);
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t pk[PER];
+    int n_bad = 0;
+    // this lane's ids first: one memory latency for all of them
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        const int q = q0 + it * kWave + lane;
+        pk[it] = q < Q ? (uint32_t)ids[q] : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        const int q = q0 + it * kWave + lane;
+        const bool inq = q < Q;
+        int e = (int)pk[it];
+        const bool inrange = inq && e >= 0 && e < E;
+        uint64_t peers = __ballot(inrange);
+        for (int b = 0; b < ebits; ++b) {
+            const bool bit = inrange && ((e >> b) & 1);
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        // duplicate: an earlier slot of the same token holds the same expert
+        // (slots before this 64-route step are read back from memory)
+        bool dup = false;
+        if (inrange) {
+            const int t = q / k, j = q - t * k;
+            const int first = lane - j;
+            dup = (peers & lt & ~((first > 0) ? (~0ull >> (64 - first)) : 0ull)) != 0;
+            for (int jj = 0; !dup && jj < -first; ++jj) dup = ids[t * k + jj] == e;
+        }
+        if (inq && (!inrange || dup)) {
+            e = -2;
+            ++n_bad;
+        }
+        peers &= ~__ballot(dup);
+        int r = 0;
+        if (e >= 0) {
+            const int before = __popcll(peers & lt);
+            r = wh[e] + before;          // every lane reads before any lane writes
+            if (before == 0) wh[e] += __popcll(peers);
+        }
+        pk[it] = inq ? ((uint32_t)(e + 2) << 21) | (uint32_t)r : 0u;
+    }
+    const int wave_bad = wave_sum_i32(n_bad);
+    if (wave_bad && lane == 0) atomicAdd(&ctrl[CTRL_BAD_ROUTES], wave_bad);
+    __syncthreads();
+
+    // per-expert totals (wave bases in place), kept counts and tiles, scans
+    int32_t kept = 0, tiles = 0;
+    for (int e = tid; e < E; e += kSmallThreads) {   // E <= 1024: one expert per thread
+        int32_t run = 0;
+        for (int w = 0; w < kSmallWaves; ++w) {
+            const int32_t c = hist[w * E + e];
+            hist[w * E + e] = run;
+            run += c;
+        }
+        counts[e] = run;
+        kept = run < C ? run : C;
+        tiles = (kept + bm - 1) / bm;
+    }
+    const int32_t off_e = block_exclusive_scan_1024(kept, s_wsum[0], &s_tot[0]);
+    const int32_t mt_e = block_exclusive_scan_1024(tiles, s_wsum[1], &s_tot[1]);
+    if (tid < E) {
+        offsets[tid] = off_e;
+        mt_off[tid] = mt_e;
+        s_off[tid] = off_e;
+    }
+    if (tid == 0) {
+        offsets[E] = s_tot[0];
+        mt_off[E] = s_tot[1];
+        s_off[E] = s_tot[0];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        const int q = q0 + it * kWave + lane;
+        if (q >= Q) continue;
+        const uint32_t w = pk[it];
+        const int e = (int)(w >> 21) - 2;
+        int32_t row = -2;
+        if (e >= 0) {
+            const int32_t r = hist[wv * E + e] + (int32_t)(w & 0x1FFFFFu);
+            row = r < C ? s_off[e] + r : -1;
+            if (row >= 0) row_src[row] = q;
+        }
+        route_dst[q] = row;
+    }
+    for (int64_t r = s_off[E] + tid; r < r_max; r += kSmallThreads) row_src[r] = -1;
+}
+
+// Row copies of placed routes: one block per token stores its row (read
+// once) to every kept row of its routes (route_dst >= 0).
+__global__ __launch_bounds__(256) void copy_rows_kernel(const uint4* __restrict__ x, int H_vec, int k,
+                                                        const int32_t* __restrict__ route_dst,
+                                                        uint4* __restrict__ x_disp) {
+    __shared__ int32_t s_row[32];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    if (tid < k) s_row[tid] = route_dst[(int64_t)t * k + tid];
+    __syncthreads();
+    const uint4* src = x + (int64_t)t * H_vec;
+    for (int c = tid; c < H_vec; c += blockDim.x) {
+        const uint4 v = src[c];
+        for (int j = 0; j < k; ++j) {
+            const int32_t row = s_row[j];
+            if (row >= 0) x_disp[(int64_t)row * H_vec + c] = v;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_copy_u32(void* dst, const void* src, int64_t n, hipStream_t s) {
@@ -621,6 +756,35 @@ hipError_t launch_count_rank(const int32_t* ids, int T, int k, int E, int C, int
     hipLaunchKernelGGL(count_rank_kernel, dim3(nb), dim3(kWave * kCountWaves), lds, s, ids, Q, k, E,
                        ebits, C, bm, rexp, lrank, partial, counts, offsets, mt_off, ctrl, route_dst,
                        row_src, r_max, delay);
+    return hipGetLastError();
+}
+
+hipError_t launch_count_place(const int32_t* ids, int T, int k, int E, int C, int bm,
+                              int32_t* counts, int32_t* offsets, int32_t* mt_off, int32_t* row_src,
+                              int64_t r_max, int32_t* route_dst, int32_t* ctrl, hipStream_t s) {
+    const int64_t Q = (int64_t)T * k;
+    if (Q <= 0 || Q > kPlaceMaxQ) return hipErrorInvalidValue;
+    int ebits = 1;
+    while ((1 << ebits) < E) ++ebits;
+    const size_t lds = sizeof(int32_t) * ((size_t)kSmallWaves * E + E + 1);
+    const int per = (int)((Q + kSmallThreads - 1) / kSmallThreads);   // routes per lane
+    auto go = [&](auto per_c) {
+        constexpr int PER = decltype(per_c)::value;
+        hipLaunchKernelGGL((count_place_kernel<PER>), dim3(1), dim3(kSmallThreads), lds, s, ids, (int)Q, k,
+                           E, ebits, C, bm, counts, offsets, mt_off, row_src, r_max, route_dst, ctrl);
+    };
+    static_assert(kPlaceMaxQ <= 4 * kSmallThreads, "at most 4 routes per lane");
+    if (per <= 2) go(std::integral_constant<int, 2>{});
+    else go(std::integral_constant<int, 4>{});
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const void* x, int T, int H, int k, int elem_bytes, const int32_t* route_dst,
+                            void* x_disp, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const int H_vec = (int)((int64_t)H * elem_bytes / 16);   // H * elem_bytes is a multiple of 256
+    hipLaunchKernelGGL(copy_rows_kernel, dim3(T), dim3(256), 0, s, (const uint4*)x, H_vec, k, route_dst,
+                       (uint4*)x_disp);
     return hipGetLastError();
 }
 

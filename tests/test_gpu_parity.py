@@ -253,8 +253,11 @@ def test_dispatch_dense_malformed_routes(k):
 
 
 def test_dispatch_ragged_blocks_and_max_k():
-    # route counts around the 2048-route block boundary, k = 32, E = 1024
-    for T, E, k, C in ((2049 // 8 + 1, 128, 8, 7), (64, 1024, 32, 3), (4097, 33, 1, 4097)):
+    # route counts around the 2048-route block boundary, k = 32, E = 1024; up
+    # to 4096 routes one workgroup places them all (4096 exactly: 4 per lane),
+    # above that the count kernel hands its totals to its last block
+    for T, E, k, C in ((2049 // 8 + 1, 128, 8, 7), (64, 1024, 32, 3), (4097, 33, 1, 4097),
+                       (512, 100, 8, 30), (8300, 64, 8, 2000)):
         _say("dispatch ragged", T, E, k, C)
         cs = synth.Case("rag", T=T, H=128, E=E, k=k, I=128, C=C, seed=T)
         ids, _ = oracle.route(synth.make_logits(cs).numpy(), k)
