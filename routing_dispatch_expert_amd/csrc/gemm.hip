@@ -24,7 +24,18 @@
 // k-tile (64 KB) is in flight while the other is multiplied, one barrier
 // per k-tile; an XOR chunk swizzle keeps the fragment reads free of bank
 // conflicts.  The ring runs on across the tiles of a workgroup (the next
-// tile's first k-tile loads during the current tile's last one).  Rows of a tile past the end of its
+// tile's first k-tile loads during the current tile's last one).
+//
+// Tiles of at most 32 rows (light experts: almost pure weight streaming) use
+// another layout of the same LDS: 3 stages of 36 KB (4 KB of A rows, 32 KB of
+// weights), so two k-tiles of weights are in flight instead of one; the ring
+// runs on across tiles of the same layout and restarts at a change.  In a
+// batch that mixes such experts with heavy ones (more than 256 rows), the
+// workgroups of odd XCDs take their tiles in descending order, so that while
+// half the chip multiplies heavy experts' tiles (MFMA-bound) the other half
+// streams light experts' weights (HBM-bound).  Either change alone measured
+// no faster on the skewed workload; both together took it from 3838 to 3505
+// us per layer.  Rows of a tile past the end of its
 // expert cost neither loads (16-row groups) nor MFMAs (32-row blocks).  bf16
 // results are regrouped in a small per-wave LDS patch so that stores write
 // 64 contiguous bytes per row.
@@ -206,8 +217,27 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int GA = BM / DR / NW;             // A row groups (DR rows) per wave: 2 or 4
     static_assert(!OUT_IN_RING || NW * 32 * kOutPitch <= A_ST, "output patch fits in an A stage");
     static_assert(!WIDE || NW == 8, "the 128-byte-row plan is laid out for 8 waves");
-    __shared__ __attribute__((aligned(1024))) unsigned char sA[STG][A_ST];
-    __shared__ __attribute__((aligned(1024))) unsigned char sB[STG][B_ST];
+    // bf16 ring layouts in one arena: 2 stages of 64 KB (A 32 KB, then B 32 KB)
+    // for tiles of more than 32 rows, 3 stages of 36 KB (A 4 KB for at most 32
+    // rows, then B 32 KB) for lighter tiles, which then keep two k-tiles of
+    // weights in flight instead of one.  e4m3: 3 stages, the A stages first.
+    constexpr int LSTG = 3, LSTAGE = 4096 + W_STAGE;
+    constexpr int RING_BYTES = WIDE ? 2 * 2 * W_STAGE : STG * (A_ST + B_ST);
+    static_assert(!WIDE || LSTG * LSTAGE <= RING_BYTES, "light stages fit the arena");
+    __shared__ __attribute__((aligned(1024))) unsigned char sRing[RING_BYTES];
+    // stage bases; the layout (light or not) is a compile-time argument
+    auto slotA = [&](auto lt_c, int slot) -> unsigned char* {
+        constexpr bool LT = decltype(lt_c)::value;
+        if (!WIDE) return sRing + slot * A_ST;
+        return sRing + (LT ? slot * LSTAGE : slot * 2 * W_STAGE);
+    };
+    auto slotB = [&](auto lt_c, int slot) -> unsigned char* {
+        constexpr bool LT = decltype(lt_c)::value;
+        if (!WIDE) return sRing + STG * A_ST + slot * B_ST;
+        return sRing + (LT ? slot * LSTAGE + 4096 : slot * 2 * W_STAGE + W_STAGE);
+    };
+    using Heavy = std::false_type;
+    using Light = std::true_type;
     __shared__ int32_t s_mt[kMaxGroupsLds + 1], s_off[kMaxGroupsLds + 1];
     __shared__ __attribute__((aligned(16))) unsigned char sOut[OUT_IN_RING ? 1 : NW][OUT_IN_RING ? 16 : 32 * kOutPitch];
     // EPI_COMBINE: the tile's routes and their weights, loaded during the
@@ -233,6 +263,18 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     }
     const int ntl = a.n_tiles;
     const int64_t total = (int64_t)total_mt * ntl;
+    // a batch mixing light experts (at most 32 rows: weight streaming) with
+    // heavy ones (more than 256 rows: MFMA-bound)
+    bool mixed = false;
+    if (WIDE && !uniform) {
+        int lt = 0, hv = 0;
+        for (int i = tid; i < a.n_groups; i += NT) {
+            const int n = s_off[i + 1] - s_off[i];
+            lt |= n > 0 && n <= 32;
+            hv |= n > 256;
+        }
+        mixed = __syncthreads_or(lt) && __syncthreads_or(hv);
+    }
 
     // Tiles are ordered (group, n-tile, m-tile) with the m-tile fastest, and
     // consecutive tile indices go to workgroups of one XCD (workgroups are
@@ -244,8 +286,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     const char* Ab = (const char*)a.A;
     const char* Bb = (const char*)a.B;
     const int nk = a.K / BKT;
-    // ring slot of a running k-tile count
-    auto ring = [](int x) { return (STG & (STG - 1)) == 0 ? (x & (STG - 1)) : (x % STG); };
 
     // DMA plan.  A: wave w fills the DR-row groups w + NW*i (row DR*group +
     // lane/(RB/16)), i < GA; with 8 waves a group wholly past the expert's
@@ -258,12 +298,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     auto swzr = [](int r) { return WIDE ? swz8(r) : swz(r); };
 
     // wave-uniform LDS bases of this wave's DMA blocks in ring slot 0
-    const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(sA[0]) + wave * 1024);
     const uint32_t rq0 = __builtin_amdgcn_readfirstlane(lds_addr(s_rq) + wave * 256);
+    // this wave's DMA bases in the arena (wave-uniform); a stage adds its offset
+    const uint32_t la0 = __builtin_amdgcn_readfirstlane(lds_addr(sRing) + wave * 1024);
+    const uint32_t lb0 = __builtin_amdgcn_readfirstlane(lds_addr(sRing) + wave * LB * 1024);
     const uint32_t rw0 = __builtin_amdgcn_readfirstlane(lds_addr(s_rw) + wave * 256);
     // routes of the epilogue staged in LDS: needs k-tiles 1, 5 and 9 (see the k-loop)
     const bool route_pf = EPI == EPI_COMBINE && nk >= 10;
-    const uint32_t lb0 = __builtin_amdgcn_readfirstlane(lds_addr(sB[0]) + wave * LB * 1024);
     static_assert(!WIDE || GA * NW * DR == BM, "A row groups cover the tile");
 
     // A tile's place in the problem and this thread's DMA sources (byte
@@ -274,6 +315,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     // B rows are consecutive weight rows, so instruction b adds 8 b rows.
     struct Tile {
         int g, nt, a_row0, rows, rot, la, lbv;
+        int light;              // bf16 tile of at most 32 rows: the 3-stage light layout
         int64_t ga[WIDE ? 1 : GA];
         int32_t ar[WIDE ? GA : 1];
         int64_t gbase;          // the expert's weights (wave-uniform)
@@ -364,6 +406,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
         // fetched into L2 once and reused.  rot depends only on the expert, so
         // a row's summation order never depends on the other tokens.
         t.rot = (g * 13) % nk;
+        t.light = WIDE && rows <= 32;
         if (WIDE) {
             int la = 0;
 #pragma unroll
@@ -375,13 +418,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
         return t;
     };
     // Load k-tile s (in the tile's own K order) of tile t into ring slot `slot`.
-    auto issue = [&](const Tile& t, int s, int slot) {
+    auto issue = [&](auto lt_c, const Tile& t, int s, int slot) {
         int kr = s + t.rot;
         if (kr >= nk) kr -= nk;
         const int k0 = kr * BKT;
         const int seg = k0 / a.k_seg;
         const int64_t bo = (int64_t)seg * a.b_seg_stride + (k0 - seg * a.k_seg);
-        const uint32_t la = la0 + slot * A_ST, lb = lb0 + slot * B_ST;
+        const uint32_t la = la0 + (uint32_t)(slotA(lt_c, slot) - sRing);
+        const uint32_t lb = lb0 + (uint32_t)(slotB(lt_c, slot) - sRing);
         if (WIDE) {
 #pragma unroll
             for (int i = 0; i < GA; ++i)
@@ -411,12 +455,24 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     // Every wait bounds the number of this thread's DMA instructions issued
     // after the awaited k-tile; other outstanding loads and stores (the
     // next tile's row lookups, the epilogue's stores) only make it stricter.
-    int64_t Lt = vid;
-    if (Lt >= total) return;  // workgroup-uniform; nothing in flight
-    Tile cur = make_tile(Lt);
+    // This workgroup's tiles are vid + i G (i < n_mine).  In a batch mixing
+    // light and heavy experts the workgroups of odd XCDs take theirs in
+    // descending order, so that while half the chip multiplies heavy experts'
+    // tiles the other half streams light experts' weights.
+    if (vid >= total) return;  // workgroup-uniform; nothing in flight
+    const int64_t n_mine = (total - 1 - vid) / G + 1;
+    const bool reverse = mixed && (blockIdx.x & 1);
+    auto tile_at = [&](int64_t i) { return (int64_t)vid + (reverse ? n_mine - 1 - i : i) * G; };
+    auto stages = [](bool light) { return FP8 ? 3 : (light ? LSTG : 2); };
+    auto ringS = [](int x, int S) { return S == 2 ? (x & 1) : x % 3; };
+    Tile cur = make_tile(tile_at(0));
     int sbase = 0;
-#pragma unroll
-    for (int st = 0; st < STG - 1; ++st) issue(cur, st, st);   // nk >= STG - 1 (K >= 128)
+    // first k-tiles (nk >= 2: K >= 128)
+    if (cur.light) {
+        for (int st = 0; st < LSTG - 1; ++st) issue(Light{}, cur, st, st);
+    } else {
+        for (int st = 0; st < STG - 1; ++st) issue(Heavy{}, cur, st, st);
+    }
 
     const int rA = lane & 31, half = lane >> 5;
     // This lane's fragment rows are rA plus multiples of 32, and swz depends on
@@ -430,10 +486,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     int loffw[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) loffw[ks] = rA * 128 + (((2 * ks + half) ^ swz8(rA)) * 16);
-    for (; Lt < total; Lt += G) {
-        const bool has_next = Lt + G < total;
-        const Tile nxt = has_next ? make_tile(Lt + G) : cur;
-        const int cn = has_next ? LB + AM * nxt.la : 0;   // next tile's DMA count per k-tile
+    for (int64_t it = 0; it < n_mine; ++it) {
+        const bool has_next = it + 1 < n_mine;
+        const Tile nxt = has_next ? make_tile(tile_at(it + 1)) : cur;
+        const int S = stages(cur.light);
+        // the ring runs on into the next tile only when it has the same layout
+        const bool chain = has_next && nxt.light == cur.light;
+        const int lc = (cur.lbv ? LB : 0) + AM * cur.la;                // this tile's DMA count per k-tile
+        const int cn = chain ? (nxt.lbv ? LB : 0) + AM * nxt.la : 0;    // and the next tile's
         const int g = cur.g, nt = cur.nt, a_row0 = cur.a_row0, rows = cur.rows;
 
         f32x16 acc[4][NBW];
@@ -452,27 +512,28 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
 
         // the pipelined k-loop, specialised on the number NA of active row
         // blocks of the wave's MFMAs and the number LA of A groups it loads
-        auto kloop = [&](auto na_c, auto la_c) {
+        auto kloop = [&](auto na_c, auto la_c, auto lt_c) {
             constexpr int NA = decltype(na_c)::value;
             constexpr int LA = decltype(la_c)::value;
             constexpr int LC = LB + AM * LA;   // this tile's DMA count per k-tile
+            constexpr bool LT = decltype(lt_c)::value;
+            constexpr int SS = FP8 ? 3 : (LT ? LSTG : 2);   // stages of this layout
             for (int kt = 0; kt < nk; ++kt) {
                 // in flight behind k-tile kt: k-tiles kt + 1 .. kt + STG - 2, of
                 // this tile or (at the end) of the next one
-                if (STG == 2) {
+                if (SS == 2) {
                     // nothing is issued after k-tile kt before this wait
                     waitcnt_barrier<0>();
-                } else if (STG == 4) {
-                    if (kt + 2 < nk) waitcnt_barrier<2 * LC>();
-                    else if (kt + 2 == nk) wait_barrier_dyn(LC + cn);
-                    else wait_barrier_dyn(2 * cn);
-                } else {
+                } else if (FP8) {
                     if (kt + 1 < nk) waitcnt_barrier<LC>();
                     else wait_barrier_dyn(cn);
+                } else {
+                    // light layout: k-tile kt + 1 (this tile's, or the next tile's first) is behind it
+                    wait_barrier_dyn(kt + 1 < nk ? lc : cn);
                 }
-                const int s = kt + STG - 1;
-                if (s < nk) issue(cur, s, ring(sbase + s));
-                else if (has_next) issue(nxt, s - nk, ring(sbase + s));
+                const int s = kt + SS - 1;
+                if (s < nk) issue(lt_c, cur, s, (sbase + s) % SS);
+                else if (chain) issue(lt_c, nxt, s - nk, (sbase + s) % SS);
                 if (EPI == EPI_COMBINE && route_pf && wave < 4) {
                     // waves 0..3 stage the routes of tile rows 64 wave + lane at
                     // k-tile 1 (every wave has left the previous tile's
@@ -486,15 +547,15 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
                     }
                 }
                 if (NA == 0) continue;
-                const int slot = ring(sbase + kt);
-                const unsigned char* sb = sB[slot];
+                const int slot = (sbase + kt) % SS;
+                const unsigned char* sb = slotB(lt_c, slot);
 #pragma unroll
                 for (int ks = 0; ks < BKT / 16; ++ks) {
                     // this lane's k = 16 ks + 8 half .. + 7: logical 16-byte chunk c
                     // of the 64-byte A half ks / 2 and of a bf16 B row; in an e4m3
                     // B row, the 8-byte piece `half` of chunk ks
                     const int lo = WIDE ? loffw[ks] : ((ks & 1) ? loff1 : loff0);   // chunk c = 2 (ks & 1) + half
-                    const unsigned char* sa = sA[slot] + (WIDE ? 0 : (ks >> 1) * A_STAGE);
+                    const unsigned char* sa = slotA(lt_c, slot) + (WIDE ? 0 : (ks >> 1) * A_STAGE);
                     bf16x8 bv[NBW], av[NA > 0 ? NA : 1];
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb) {
@@ -518,11 +579,26 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
             }
         };
         auto by_la = [&](auto na_c) {
-            if (WIDE) kloop(na_c, std::integral_constant<int, 0>{});       // waits need no DMA count
-            else if (NW != 8) kloop(na_c, std::integral_constant<int, GA>{});   // every A group loaded
-            else if (cur.la == 2) kloop(na_c, std::integral_constant<int, 2>{});
-            else if (cur.la == 1) kloop(na_c, std::integral_constant<int, 1>{});
-            else kloop(na_c, std::integral_constant<int, 0>{});
+            constexpr int NA = decltype(na_c)::value;
+            if constexpr (WIDE) {
+                // waits need no compile-time DMA count; a light tile has at
+                // most one active row block
+                if constexpr (NA <= 1) {
+                    if (cur.light) {
+                        kloop(na_c, std::integral_constant<int, 0>{}, Light{});
+                        return;
+                    }
+                }
+                kloop(na_c, std::integral_constant<int, 0>{}, Heavy{});
+            } else if (NW != 8) {
+                kloop(na_c, std::integral_constant<int, GA>{}, Heavy{});   // every A group loaded
+            } else if (cur.la == 2) {
+                kloop(na_c, std::integral_constant<int, 2>{}, Heavy{});
+            } else if (cur.la == 1) {
+                kloop(na_c, std::integral_constant<int, 1>{}, Heavy{});
+            } else {
+                kloop(na_c, std::integral_constant<int, 0>{}, Heavy{});
+            }
         };
         switch (n_act) {
             case 4: by_la(std::integral_constant<int, 4>{}); break;
@@ -544,7 +620,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
             // multiplied (its LDS reads are complete before the barrier); its
             // slot is refilled only after the next tile's first barrier
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            so = sA[ring(sbase + nk - 1)] + wave * 32 * kOutPitch;
+            so = slotA(Heavy{}, ringS(sbase + nk - 1, S)) + wave * 32 * kOutPitch;
         } else {
             so = sOut[wave];
         }
@@ -631,7 +707,21 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
                 }
             }
         }
-        sbase = ring(sbase + nk);
+        if (!has_next) break;
+        if (chain) {
+            sbase = ringS(sbase + nk, S);
+        } else {
+            // the next tile takes the other layout and nothing of it was
+            // issued: once every wave is past its last reads of this tile's
+            // stages, its first k-tiles start a fresh ring
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            sbase = 0;
+            if (nxt.light) {
+                for (int st = 0; st < LSTG - 1; ++st) issue(Light{}, nxt, st, st);
+            } else {
+                for (int st = 0; st < STG - 1; ++st) issue(Heavy{}, nxt, st, st);
+            }
+        }
         cur = nxt;
     }
 }
