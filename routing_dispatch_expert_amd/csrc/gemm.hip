@@ -464,7 +464,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     const bool reverse = mixed && (blockIdx.x & 1);
     auto tile_at = [&](int64_t i) { return (int64_t)vid + (reverse ? n_mine - 1 - i : i) * G; };
     auto stages = [](bool light) { return FP8 ? 3 : (light ? LSTG : 2); };
-    auto ringS = [](int x, int S) { return S == 2 ? (x & 1) : x % 3; };
+    auto ringS = [](int x, int S) { return S == 2 ? (x & 1) : (int)((unsigned)x % 3u); };
     Tile cur = make_tile(tile_at(0));
     int sbase = 0;
     // first k-tiles (nk >= 2: K >= 128)
@@ -518,6 +518,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
             constexpr int LC = LB + AM * LA;   // this tile's DMA count per k-tile
             constexpr bool LT = decltype(lt_c)::value;
             constexpr int SS = FP8 ? 3 : (LT ? LSTG : 2);   // stages of this layout
+            // ring slot of a running k-tile count (non-negative: no signed modulo)
+            auto slot_of = [](int x) { return SS == 2 ? (x & 1) : (int)((unsigned)x % (unsigned)SS); };
             for (int kt = 0; kt < nk; ++kt) {
                 // in flight behind k-tile kt: k-tiles kt + 1 .. kt + STG - 2, of
                 // this tile or (at the end) of the next one
@@ -532,8 +534,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
                     wait_barrier_dyn(kt + 1 < nk ? lc : cn);
                 }
                 const int s = kt + SS - 1;
-                if (s < nk) issue(lt_c, cur, s, (sbase + s) % SS);
-                else if (chain) issue(lt_c, nxt, s - nk, (sbase + s) % SS);
+                if (s < nk) issue(lt_c, cur, s, slot_of(sbase + s));
+                else if (chain) issue(lt_c, nxt, s - nk, slot_of(sbase + s));
                 if (EPI == EPI_COMBINE && route_pf && wave < 4) {
                     // waves 0..3 stage the routes of tile rows 64 wave + lane at
                     // k-tile 1 (every wave has left the previous tile's
@@ -547,7 +549,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
                     }
                 }
                 if (NA == 0) continue;
-                const int slot = (sbase + kt) % SS;
+                const int slot = slot_of(sbase + kt);
                 const unsigned char* sb = slotB(lt_c, slot);
 #pragma unroll
                 for (int ks = 0; ks < BKT / 16; ++ks) {
@@ -575,6 +577,19 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
                         for (int nb = 0; nb < NBW; ++nb)
                             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[nb], av[mb], acc[mb][nb], 0, 0, 0);
+                    if constexpr (WIDE && NA == 4) {
+                        // keep the fragment reads ahead of the MFMAs that use them
+                        // (near the register limit the scheduler otherwise waits on
+                        // each read): B 0-1 and A 0-1, 2 MFMAs, A 2-3, 6 MFMAs
+                        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+                    } else if constexpr (WIDE && NA > 0) {
+                        // all of the step's reads, then its MFMAs
+                        __builtin_amdgcn_sched_group_barrier(0x100, NBW + NA, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, NBW * NA, 0);
+                    }
                 }
             }
         };
