@@ -52,7 +52,10 @@
  * Shapes (moe_problem fields): T tokens, H hidden, E routed experts, k top-k
  * (1 <= k <= min(E, 32)), I expert intermediate size, C capacity (rows per
  * expert).  R_max = min(T*k, E*C) is the size of the expert-contiguous
- * buffer.  H and I must be multiples of 128, and so must I_shared.
+ * buffer.  H and I must be multiples of 128, and so must I_shared
+ * (MOE_ERR_UNSUPPORTED otherwise): every expert GEMM walks K in 64-element
+ * k-tiles and its output in 128-column blocks, so no ragged K or column tail
+ * is handled.  The pages' workloads all satisfy it.
  *
  * Layouts:
  *   x        [T, H]          act_dtype
@@ -147,7 +150,13 @@ typedef struct moe_meta {
 } moe_meta;
 
 /* Workspace size in bytes for problem `p` (the same for every entry point).
- * Returns MOE_ERR_ARG for an invalid problem. */
+ * The workspace is the caller's and is reused from call to call, so that a
+ * captured launch sequence replays without allocation (PR 33963
+ * "Description": existing routing workspaces are reused; the afdEP
+ * count-first record, "setup": runs under CUDA graphs): per-block counts,
+ * route ranks, the expert-contiguous rows, the intermediate h and the
+ * token-ordered slot rows of the combine.  Returns
+ * MOE_ERR_ARG for an invalid problem. */
 moe_status moe_workspace_bytes(const moe_problem *p, size_t *bytes);
 
 /* Zero the persistent state at the head of a freshly allocated workspace
@@ -224,7 +233,12 @@ moe_status moe_combine(const moe_problem *p, const void *y_disp,
                        const float *y_shared, void *out, void *ws,
                        size_t ws_bytes, void *stream);
 
-/* The whole layer: route as moe_route does with `logits` and `score_bias`
+/* The whole layer, in the order of the fleet megakernel report's MoE steps
+ * (gate and top-k, experts, weighted combine) with the count-first dispatch
+ * of the afdEP record between routing and experts, and PR 33963's contract
+ * ("Description": internal routing or preselected FP32 ids/weights taken
+ * unchanged, BF16 store boundaries, FP32 final reduction): route as
+ * moe_route does with `logits` and `score_bias`
  * (or take ids_in / w_in, unchanged, when both are non-NULL),
  * dispatch, expert FFN with the combine weights applied in the
  * down-projection epilogue, shared experts, and the final sum to token
@@ -257,7 +271,10 @@ moe_status moe_forward_static(const moe_problem *p, const void *x, const float *
                               const float *s2, const void *w13_sh, const void *w2_sh,
                               void *out, const moe_meta *meta, void *stream);
 
-/* Synchronise `stream`, return the number of malformed routes seen since
+/* Malformed-route report (PR 33963 "Description": isolation of malformed
+ * routes, affected tokens poisoned; the afdEP record's correctness runner
+ * counts rejected routes of each invalid class).
+ * Synchronise `stream`, return the number of malformed routes seen since
  * the last call in *n_invalid_routes, and clear the counter. */
 moe_status moe_error(void *ws, size_t ws_bytes, void *stream,
                      int32_t *n_invalid_routes);
