@@ -386,22 +386,41 @@ hipError_t run_decode(const DecodeSeg* a, const DecodeSeg* b, const int32_t* row
     // a routed segment (tile table staged in LDS) can only be the first one
     if (d.n_seg > 1 && d.seg[1].offsets) return hipErrorInvalidValue;
     if (d.seg[0].offsets && (!d.seg[0].mt || d.seg[0].n_groups > kDecodeMaxGroups)) return hipErrorInvalidValue;
-    // Split K over a workgroup's 4 wavefronts when the launch has fewer units
-    // than the chip has wavefronts and each wavefront still gets >= 5 K groups
-    // of 64 (K >= 1280; shorter streams are mostly ring fill, and measured
-    // slower split than whole).  The number of touched experts is on the
-    // device; the host bounds it by min(E, T*k).
+    // When the launch has fewer units than the chip has wavefronts, split
+    // each unit's K over 2 or 4 wavefronts of a workgroup, choosing the split
+    // with the fewest K groups on the longest wavefront's path: a first round
+    // of the longest units (the shared experts' down projections go first),
+    // then rounds of the shortest, each costing its K groups per wavefront
+    // plus 4 for the ring fill, the partial sums and the epilogue; ties go to
+    // the wider split.  The number of touched experts is on the device; the
+    // host bounds it by min(E, T*k).
     int64_t units = 0;
-    int kmin = INT_MAX;
+    int kmin = INT_MAX, kmax = 0;
     for (int i = 0; i < d.n_seg; ++i) {
         const DecodeSeg& g = d.seg[i];
         const int64_t groups = g.offsets ? std::min<int64_t>(g.n_groups, route_count) : g.n_groups;
         units += groups * g.blocks;
         kmin = std::min(kmin, g.K);
+        kmax = std::max(kmax, g.K);
     }
-    const int split = (units < (int64_t)decode_grid() * 4 && kmin >= 1280) ? 1 : 0;
-    // otherwise the partial last round is split the same way (same K bound)
-    d.tail_split = !split && kmin >= 1280;
+    const int64_t waves = (int64_t)decode_grid() * 4;
+    int split = 1;
+    if (units < waves) {
+        const int64_t nk_long = kmax / 64, nk_short = kmin / 64;   // K groups of 64
+        int64_t best = -1;
+        for (int s : {4, 2, 1}) {
+            const int64_t rounds = (units + waves / s - 1) / (waves / s);
+            const int64_t cost = (nk_long + s - 1) / s + 4 + (rounds - 1) * ((nk_short + s - 1) / s + 4);
+            if (best < 0 || cost < best) {
+                best = cost;
+                split = s;
+            }
+        }
+    }
+    // otherwise the partial last round is split over a workgroup's
+    // wavefronts when each still gets >= 5 K groups of 64 (K >= 1280; shorter
+    // streams are mostly ring fill, and measured slower split than whole)
+    d.tail_split = split == 1 && kmin >= 1280;
     // the shared experts are always bf16; a segment list that starts with them
     // runs the bf16 instantiation
     const int small_m = (max_rows >= 0 && max_rows <= 8) ? 1 : 0;

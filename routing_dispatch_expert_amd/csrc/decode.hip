@@ -357,19 +357,21 @@ struct Item {
     float cw;               // and its weight
     const char* asrc[4];
     const char* bsrc[4];
+    int dummy;              // (SPL = 2) a position past the last unit: only the pair's barriers
 };
 
 // Units are numbered segment by segment; within a segment, group-major with
-// the 32-row weight blocks fastest.  SPLIT: a workgroup takes one unit at a
-// time and its wavefronts split the unit's K range (each streams a quarter of
-// the weight rows through its own ring; the partial sums meet in LDS), for
-// launches with few units.  Otherwise every wavefront takes units on its own,
+// the 32-row weight blocks fastest.  SPL = 4: a workgroup takes one unit at
+// a time and its wavefronts split the unit's K range (each streams a quarter
+// of the weight rows through its own ring; the partial sums meet in LDS), for
+// launches with few units.  SPL = 2: each pair of wavefronts takes a unit and
+// splits its K in halves.  SPL = 1: every wavefront takes units on its own,
 // dealt to workgroups first (unit u to workgroup u % grid, wavefront
 // u / grid), so that a launch with fewer units than wavefronts still spreads
 // them over every CU.  Work items exist only for experts
 // with rows (the dispatch's 32-row tile table, kept in LDS with the experts'
 // row ranges).
-template <int EPI0, int EPI1, bool FP8, bool SPLIT, bool SMALLM, bool FUSED>
+template <int EPI0, int EPI1, bool FP8, int SPL, bool SMALLM, bool FUSED>
 __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs d) {
     using RG = DRing<SMALLM>;
     __shared__ __attribute__((aligned(1024))) unsigned char rings[kDWaves][kDRing];
@@ -420,9 +422,10 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     const int64_t n0 = items(0);
     const int64_t n1 = d.n_seg > 1 ? items(1) : 0;
     const int64_t total = n0 + n1;
-    // Positions: SPLIT takes one unit per workgroup at a time (position b + G r
-    // for workgroup b), its wavefronts splitting the unit's K.  Otherwise every
-    // wavefront takes whole units (position w G + b + 4 G r for wavefront w),
+    // Positions: SPL = 4 takes one unit per workgroup at a time (position
+    // b + G r for workgroup b), its wavefronts splitting the unit's K; SPL = 2
+    // one unit per pair of wavefronts (position j G + b + 2 G r for pair j).
+    // SPL = 1: every wavefront takes whole units (position w G + b + 4 G r for wavefront w),
     // and with tail_split only the complete rounds may run that way: the last,
     // partial round (positions from tail0) is then taken one unit per
     // workgroup and split, so that a fraction of the wavefronts do not each
@@ -431,11 +434,12 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     // holds at most one unit per workgroup: larger tails cost each split unit
     // its own ring fill and measured slower.
     const int64_t WA = (int64_t)gridDim.x * kDWaves;
-    const bool hybrid = !SPLIT && d.tail_split && total >= WA && total % WA != 0 &&
+    const bool hybrid = SPL == 1 && d.tail_split && total >= WA && total % WA != 0 &&
                         total % WA <= (int64_t)gridDim.x;
     const int64_t tail0 = hybrid ? (total / WA) * WA : total;
-    const int64_t first = SPLIT ? blockIdx.x : (int64_t)wave * gridDim.x + blockIdx.x;
-    const int64_t stride = SPLIT ? gridDim.x : WA;
+    constexpr int SLOTS = kDWaves / SPL;   // units a workgroup works on at a time
+    const int64_t first = (int64_t)(wave / SPL) * gridDim.x + blockIdx.x;
+    const int64_t stride = (int64_t)SLOTS * gridDim.x;
     // Position p of the loop (slot p % stride, round p / stride) -> unit.  When
     // segment 1's units are longer (the shared experts' down projection runs
     // over their concatenated intermediates), they go to slots that get one
@@ -457,14 +461,14 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     const int dr = lane >> 3, dsl = lane & 7;   // DMA: instruction i covers rows 8i + lane/8, chunk slot lane%8
 
     // this wavefront's K range and DMA sources of the item's block m0
-    // spl: the unit is split over the workgroup's wavefronts
-    auto setup = [&](Item& it, int m0, bool spl) {
+    // ways: wavefronts sharing the unit (1, 2 or 4), each taking a 1/ways of its K
+    auto setup = [&](Item& it, int m0, int ways) {
         const DecodeSeg& s = d.seg[it.si];
         it.m0 = m0;
         it.mrows = min(kDecodeBM, it.rows - m0);
         const int nKall = s.K / kDGroupK;
-        const int kq = spl ? (nKall + kDWaves - 1) / kDWaves : nKall;
-        it.g0 = spl ? min(nKall, wave * kq) : 0;
+        const int kq = (nKall + ways - 1) / ways;
+        it.g0 = min(nKall, (wave % ways) * kq);
         it.nK = min(nKall, it.g0 + kq) - it.g0;
         // units running at the same time start at different K groups, so the
         // weight rows (a power-of-two stride apart) are not all read at the
@@ -497,8 +501,14 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
         }
     };
     // item u: segment, expert (tile table), 32-row block, weight block
-    auto make = [&](int64_t u, Item& it, bool spl) {
+    auto make = [&](int64_t u, Item& it, int ways) {
         it.u = u;                        // loop position
+        it.dummy = SPL == 2 && u >= total;
+        if (it.dummy) {
+            it.si = 0;
+            it.nK = 0;
+            return;
+        }
         const int64_t un = unit_at(u);   // the unit it holds
         it.si = un < n0 ? 0 : 1;
         const DecodeSeg& s = d.seg[it.si];
@@ -519,7 +529,7 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
             it.base = 0;
             it.rows = s.uniform_rows;
         }
-        setup(it, m0, spl);
+        setup(it, m0, ways);
         if ((it.si == 0 ? EPI0 : EPI1) == EPI_COMBINE) {
             const int m = min(lane & 31, it.mrows - 1);
             const int rr = it.base + m0 + m;
@@ -551,15 +561,22 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
 
     // The loop, once for launches that split their partial last round
     // (HYB: whether the current unit is split is a run-time state) and once
-    // for the others (fixed by SPLIT); `hybrid` is workgroup-uniform.
+    // for the others (fixed by SPL); `hybrid` is workgroup-uniform.
     auto run = [&](auto hyb_c) {
         constexpr bool HYB = decltype(hyb_c)::value;
         Item cur, nxt;
         // the phase-1 positions of every wavefront of a workgroup are equally many,
         // and the phase-2 positions are the workgroup's: both tests are
-        // workgroup-uniform where it matters (SPLIT, and the switch to phase 2)
-        bool sp = SPLIT;   // (HYB) the current unit is split over the workgroup's wavefronts
-        int64_t pstride = stride, pend = SPLIT ? total : tail0;
+        // workgroup-uniform where it matters (SPL = 4, and the switch to phase 2)
+        bool sp = SPL == 4;   // (HYB) the current unit is split over the workgroup's wavefronts
+        int64_t pstride = stride, pend = SPL == 1 ? tail0 : total;
+        if (SPL == 2) {
+            // both pairs of a workgroup take as many positions as the first
+            // pair has units (the second pair's last may be past the end), so
+            // that they meet at the same barriers
+            const int64_t r2 = blockIdx.x < total ? (total - blockIdx.x + stride - 1) / stride : 0;
+            pend = first + stride * r2;
+        }
         int64_t p0 = first;
         if (p0 >= pend) {
             if (!HYB || tail0 + blockIdx.x >= total) return;
@@ -568,7 +585,7 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
             pstride = gridDim.x;
             pend = total;
         }
-        make(p0, cur, HYB ? sp : SPLIT);
+        make(p0, cur, HYB ? (sp ? kDWaves : 1) : SPL);
         int issued = 0, consumed = 0;  // stages of this wavefront's stream
         int pre = 0;                   // stages of `cur` already issued
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -616,24 +633,26 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
             // Each wavefront's ring is idle here (its stages are all consumed), so
             // it holds the wavefront's partial sums; the second barrier keeps the
             // rings from being refilled before wavefront 0 has read them.
+            // (groups of `wy` wavefronts: the first of each group owns the unit)
             bool owner = true;
-            if (HYB ? sp : SPLIT) {
-                if (wave > 0) {
+            const int wy = HYB ? (sp ? kDWaves : 1) : SPL;
+            if (wy > 1) {
+                const int w0 = wave - wave % wy;
+                if (wave > w0) {
                     float* mine = (float*)ring;
     #pragma unroll
                     for (int r = 0; r < 16; ++r) mine[r * 64 + lane] = acc[r];
                 }
                 __syncthreads();
-                if (wave == 0) {
-    #pragma unroll
-                    for (int w = 1; w < kDWaves; ++w) {
+                if (wave == w0) {
+                    for (int w = w0 + 1; w < w0 + wy; ++w) {
                         const float* theirs = (const float*)rings[w];
     #pragma unroll
                         for (int r = 0; r < 16; ++r) acc[r] += theirs[r * 64 + lane];
                     }
                 }
                 __syncthreads();
-                owner = wave == 0;
+                owner = wave == w0 && !cur.dummy;
             }
             if (owner) {
                 if (cur.si == 0)
@@ -650,7 +669,7 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
                 pstride = gridDim.x;
                 pend = total;
             }
-            make(pn, nxt, HYB ? sp : SPLIT);
+            make(pn, nxt, HYB ? (sp ? kDWaves : 1) : SPL);
             cur = nxt;
             pre = 0;
         }
@@ -667,11 +686,16 @@ hipError_t launch_decode_gemm(const DecodeArgs& d, int w_dtype, int split, int s
     const int e0 = d.seg[0].epi;
     const int e1 = d.n_seg > 1 ? d.seg[1].epi : ((e0 == EPI_SWIGLU || e0 == EPI_RELU2) ? EPI_SWIGLU : EPI_F32);
     dim3 g(grid), b(kDWaves * 64);
+    if (split != 1 && split != 2 && split != 4) return hipErrorInvalidValue;
+    // split: wavefronts per unit
+#define RDE_L(A, B, F8, S, SM, FU) hipLaunchKernelGGL((decode_gemm_kernel<A, B, F8, S, SM, FU>), g, b, 0, st, d)
+#define RDE_S(A, B, F8, SM, FU)                    \
+    if (split == 4) RDE_L(A, B, F8, 4, SM, FU);    \
+    else if (split == 2) RDE_L(A, B, F8, 2, SM, FU); \
+    else RDE_L(A, B, F8, 1, SM, FU);
     if (d.use_fused) {
         // routing inside the launch: bf16 gate/up projections only
-#define RDE_DECF(A, SM)                                                                                           \
-    if (split) hipLaunchKernelGGL((decode_gemm_kernel<A, EPI_SWIGLU, false, true, SM, true>), g, b, 0, st, d);    \
-    else hipLaunchKernelGGL((decode_gemm_kernel<A, EPI_SWIGLU, false, false, SM, true>), g, b, 0, st, d);
+#define RDE_DECF(A, SM) RDE_S(A, EPI_SWIGLU, false, SM, true)
         if (fp8 || e1 != EPI_SWIGLU) return hipErrorInvalidValue;
         if (e0 == EPI_SWIGLU) {
             if (small_m) { RDE_DECF(EPI_SWIGLU, true) }
@@ -685,11 +709,9 @@ hipError_t launch_decode_gemm(const DecodeArgs& d, int w_dtype, int split, int s
 #undef RDE_DECF
         return hipGetLastError();
     }
-#define RDE_DEC4(A, B, SM)                                                                                     \
-    if (fp8 && split) hipLaunchKernelGGL((decode_gemm_kernel<A, B, true, true, SM, false>), g, b, 0, st, d);   \
-    else if (fp8) hipLaunchKernelGGL((decode_gemm_kernel<A, B, true, false, SM, false>), g, b, 0, st, d);      \
-    else if (split) hipLaunchKernelGGL((decode_gemm_kernel<A, B, false, true, SM, false>), g, b, 0, st, d);    \
-    else hipLaunchKernelGGL((decode_gemm_kernel<A, B, false, false, SM, false>), g, b, 0, st, d);
+#define RDE_DEC4(A, B, SM)                   \
+    if (fp8) { RDE_S(A, B, true, SM, false) }  \
+    else { RDE_S(A, B, false, SM, false) }
 #define RDE_DEC(A, B)                      \
     if (e0 == A && e1 == B) {              \
         if (small_m) { RDE_DEC4(A, B, true) } \
@@ -703,6 +725,8 @@ hipError_t launch_decode_gemm(const DecodeArgs& d, int w_dtype, int split, int s
     RDE_DEC(EPI_F32, EPI_F32)
 #undef RDE_DEC
 #undef RDE_DEC4
+#undef RDE_S
+#undef RDE_L
     return hipErrorInvalidValue;
 }
 
