@@ -647,12 +647,19 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
             // routes that fit one count block are placed by that block when no
             // rows are copied: no separate scatter launch
             const bool place = in_place && count_blocks(Q) <= 1;
+            // rows read in place and few per-block totals: the metadata
+            // scatter scans them itself
+            const int local = in_place && local_scan_fits(Q, P.E) ? 1 : 0;
             e = launch_count_rank(ids, P.T, P.k, P.E, P.C, tile_bm, at<int32_t>(ws, L.rexp),
                                   at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), counts, offsets, mt,
                                   at<int32_t>(ws, L.ctrl), s, place ? route_dst : nullptr, row_src,
-                                  r_max_of(P));
+                                  r_max_of(P), local);
             if (e == hipSuccess) e = mark(m, MOE_STAGE_COUNT, s);
-            if (e == hipSuccess && P.T > 0 && !place)
+            if (e == hipSuccess && P.T > 0 && !place && local)
+                e = launch_scatter_scan(P.T, P.k, P.E, P.C, tile_bm, r_max_of(P), at<int32_t>(ws, L.rexp),
+                                        at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.partial), counts, offsets,
+                                        mt, route_dst, row_src, s);
+            else if (e == hipSuccess && P.T > 0 && !place)
                 e = launch_scatter(x, P.T, P.H, P.k, P.E, P.C, act_bytes(P), r_max_of(P),
                                    at<int32_t>(ws, L.rexp), at<int32_t>(ws, L.lrank),
                                    at<int32_t>(ws, L.partial), offsets, route_dst, row_src,

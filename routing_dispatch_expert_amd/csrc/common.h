@@ -64,11 +64,31 @@ hipError_t launch_route(const float* logits, const float* bias, int T, int E, in
 // With route_dst given and at most kCountBlock routes (one block), the kernel
 // also places the routes (route_dst, row_src with -1 from the kept rows up to
 // r_max), so no metadata scatter is needed.
+// local_scan (several blocks, local_scan_fits): the blocks only publish
+// their totals in partial and launch_scatter_scan does the rest.
 hipError_t launch_count_rank(const int32_t* ids, int T, int k, int E, int C, int bm,
                              int32_t* rexp, int32_t* lrank, int32_t* partial,
                              int32_t* counts, int32_t* offsets, int32_t* mt_off,
                              int32_t* ctrl, hipStream_t s, int32_t* route_dst = nullptr,
-                             int32_t* row_src = nullptr, int64_t r_max = 0);
+                             int32_t* row_src = nullptr, int64_t r_max = 0, int local_scan = 0);
+
+// Several count blocks whose per-block totals (blocks x experts words) are
+// few enough for every block of the metadata scatter to scan them itself:
+// the count kernel then needs no hand-off between its blocks (its ticket,
+// the write-through totals and the last block's scan cost more than each
+// scatter block reading the totals from L2: 16384 routes over 128 experts,
+// count 11.8 -> 8.0 us, metadata scatter 3.8 -> 4.1 us).
+constexpr int kLocalScanMax = 2048;
+inline bool local_scan_fits(int64_t Q, int E) {
+    const int nb = count_blocks(Q);
+    return nb > 1 && (int64_t)nb * E <= kLocalScanMax;
+}
+// After launch_count_rank(..., local_scan = 1), for the expert GEMMs that
+// read rows in place: per-block bases, counts, offsets, the m-tile table
+// (tile rows bm), route_dst and row_src (-1 from the kept rows up to r_max).
+hipError_t launch_scatter_scan(int T, int k, int E, int C, int bm, int64_t r_max, const int32_t* rexp,
+                               const int32_t* lrank, const int32_t* cnt, int32_t* counts, int32_t* offsets,
+                               int32_t* mt_off, int32_t* route_dst, int32_t* row_src, hipStream_t s);
 
 // At most kPlaceMaxQ routes: one 1024-thread workgroup ranks every route,
 // writes counts, offsets and the m-tile table, and places every route

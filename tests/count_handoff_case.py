@@ -2,9 +2,11 @@
 set in its environment (the library reads it once): block 0 of the count
 kernel holds back its arrival ticket, so it is the last block to arrive and
 the one that reads every other block's write-through totals and scans them.
-moe_dispatch (with the row copy) and moe_forward on batches of more than
-4096 routes (below that one workgroup places every route and there is no
-hand-off) must still match the oracle bit for bit on their metadata.  Prints "ok" on success."""
+moe_dispatch (with the row copy) on more than 4096 routes (below that one
+workgroup places every route) and moe_forward on batches whose per-block
+totals also number more than 2048 (below that the metadata scatter scans
+them itself and the count blocks hand nothing over) must still match the
+oracle bit for bit on their metadata.  Prints "ok" on success."""
 import os
 import sys
 
@@ -21,8 +23,8 @@ from gpu_helpers import DEV, np_i32, parity_case, problem, r_max, workspace  # n
 
 
 def dispatch_case():
-    # 2100 tokens x top-8 = 16800 routes: 9 count blocks with the hand-off
-    cs = parity_case("prefill_T2048", T=2100, H=256, E=64, k=8, I=128, C=300)
+    # 2100 tokens x top-8 = 16800 routes: 9 count blocks x 256 experts, with the hand-off
+    cs = parity_case("prefill_T2048", T=2100, H=256, E=256, k=8, I=128, C=300)
     print("[case] dispatch", cs.T, cs.E, cs.k, flush=True)
     x = synth.make_x(cs)
     ids, _ = oracle.route(synth.make_logits(cs).numpy(), cs.k)
@@ -47,7 +49,8 @@ def dispatch_case():
 
 
 def forward_case():
-    cs = parity_case("prefill_T256", T=600, H=256, E=16, k=8, I=128, C=200)
+    # 4800 routes: 3 count blocks x 1024 experts
+    cs = parity_case("prefill_T256", T=600, H=256, E=1024, k=8, I=128, C=200)
     print("[case] forward", cs.T, cs.E, cs.k, flush=True)
     inp = synth.make_inputs(cs, DEV)
     p = problem(cs)
