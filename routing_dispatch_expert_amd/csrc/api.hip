@@ -417,6 +417,12 @@ hipError_t run_decode(const DecodeSeg* a, const DecodeSeg* b, const int32_t* row
             }
         }
     }
+    // MOE_DECODE_SPLIT = 1, 2 or 4 (read on every call) forces the split of
+    // every decode launch, so tests can run each form over several rounds
+    if (const char* f = std::getenv("MOE_DECODE_SPLIT")) {
+        const int v = std::atoi(f);
+        if (v == 1 || v == 2 || v == 4) split = v;
+    }
     // otherwise the partial last round is split over a workgroup's
     // wavefronts when each still gets >= 5 K groups of 64 (K >= 1280; shorter
     // streams are mostly ring fill, and measured slower split than whole)
