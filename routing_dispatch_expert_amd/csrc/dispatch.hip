@@ -21,7 +21,15 @@
 // base[block][e] + its in-block rank; a rank below C places the route at row
 // offsets[e] + rank.  The token's row is read once and stored to each of its
 // kept rows with 16-byte vector stores.  When no row copy is asked for, a
-// metadata-only variant takes one thread per route.
+// metadata-only variant takes one thread per route; when the per-block
+// totals are few (blocks x experts <= kLocalScanMax), that variant's blocks
+// each scan the totals themselves and the count blocks hand nothing over.
+//
+// Batches of at most 4096 routes skip the hand-off altogether: one
+// 1024-thread workgroup counts, ranks, scans and places every route
+// (count_place), and copy_rows then copies the rows when a copy is wanted.
+// Batches of at most 64 tokens on the decode path are routed and dispatched
+// by one workgroup (small_dispatch).
 #include <algorithm>
 #include <cstdlib>
 #include <type_traits>
