@@ -19,9 +19,10 @@
 // The MFMA is issued as W x A^T: lane l holds activation row (l % 32) and
 // weight rows n = 8*(r/4) + 4*(l/32) + r%4 for acc register r.
 //
-// For launches with few units, a workgroup of 4 wavefronts works on one unit
-// at a time, each wavefront on a quarter of K; the four partial sums are
-// added in LDS in wavefront order.
+// For launches with few units, the 4 wavefronts of a workgroup work on one
+// unit at a time, each on a quarter of K, or each pair of wavefronts on one
+// unit, each on half of K (the host chooses from the unit count and K); the
+// partial sums are added in LDS in wavefront order.
 //
 // K order: a work item starts at K group (13 expert + 7 block) mod its group
 // count and wraps (see Item::rot).
