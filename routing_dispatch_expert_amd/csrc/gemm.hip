@@ -26,11 +26,13 @@
 // conflicts.  The ring runs on across the tiles of a workgroup (the next
 // tile's first k-tile loads during the current tile's last one).
 //
-// Tiles of at most 32 rows (light experts: almost pure weight streaming) use
-// another layout of the same LDS: 3 stages of 36 KB (4 KB of A rows, 32 KB of
+// Tiles of at most 64 rows (light experts: mostly weight streaming) use
+// another layout of the same LDS: 3 stages of 40 KB (8 KB of A rows, 32 KB of
 // weights), so two k-tiles of weights are in flight instead of one; the ring
-// runs on across tiles of the same layout and restarts at a change.  In a
-// batch that mixes such experts with heavy ones (more than 256 rows), the
+// runs on across tiles of the same layout and restarts at a change.  (Tiles
+// of 33 to 64 rows went from 170 to 120 us in the gate/up GEMM of the skewed
+// workload with it.)  In a batch that mixes experts of at most 32 rows with
+// heavy ones (more than 256 rows), the
 // workgroups of odd XCDs take their tiles in descending order, so that while
 // half the chip multiplies heavy experts' tiles (MFMA-bound) the other half
 // streams light experts' weights (HBM-bound).  Either change alone measured
@@ -218,10 +220,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     static_assert(!OUT_IN_RING || NW * 32 * kOutPitch <= A_ST, "output patch fits in an A stage");
     static_assert(!WIDE || NW == 8, "the 128-byte-row plan is laid out for 8 waves");
     // bf16 ring layouts in one arena: 2 stages of 64 KB (A 32 KB, then B 32 KB)
-    // for tiles of more than 32 rows, 3 stages of 36 KB (A 4 KB for at most 32
+    // for tiles of more than 64 rows, 3 stages of 40 KB (A 8 KB for at most 64
     // rows, then B 32 KB) for lighter tiles, which then keep two k-tiles of
     // weights in flight instead of one.  e4m3: 3 stages, the A stages first.
-    constexpr int LSTG = 3, LSTAGE = 4096 + W_STAGE;
+    constexpr int LSTG = 3, LSTAGE = 8192 + W_STAGE;
     constexpr int RING_BYTES = WIDE ? 2 * 2 * W_STAGE : STG * (A_ST + B_ST);
     static_assert(!WIDE || LSTG * LSTAGE <= RING_BYTES, "light stages fit the arena");
     __shared__ __attribute__((aligned(1024))) unsigned char sRing[RING_BYTES];
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     auto slotB = [&](auto lt_c, int slot) -> unsigned char* {
         constexpr bool LT = decltype(lt_c)::value;
         if (!WIDE) return sRing + STG * A_ST + slot * B_ST;
-        return sRing + (LT ? slot * LSTAGE + 4096 : slot * 2 * W_STAGE + W_STAGE);
+        return sRing + (LT ? slot * LSTAGE + 8192 : slot * 2 * W_STAGE + W_STAGE);
     };
     using Heavy = std::false_type;
     using Light = std::true_type;
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
     // B rows are consecutive weight rows, so instruction b adds 8 b rows.
     struct Tile {
         int g, nt, a_row0, rows, rot, la, lbv;
-        int light;              // bf16 tile of at most 32 rows: the 3-stage light layout
+        int light;              // bf16 tile of at most 64 rows: the 3-stage light layout
         int64_t ga[WIDE ? 1 : GA];
         int32_t ar[WIDE ? GA : 1];
         int64_t gbase;          // the expert's weights (wave-uniform)
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
         // fetched into L2 once and reused.  rot depends only on the expert, so
         // a row's summation order never depends on the other tokens.
         t.rot = (g * 13) % nk;
-        t.light = WIDE && rows <= 32;
+        t.light = WIDE && rows <= 64;
         if (WIDE) {
             int la = 0;
 #pragma unroll
@@ -596,8 +598,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
         auto by_la = [&](auto na_c) {
             constexpr int NA = decltype(na_c)::value;
             if constexpr (WIDE) {
-                // waits need no compile-time DMA count; a light tile has at
-                // most one active row block
+                // waits need no compile-time DMA count; on a light tile a
+                // wave has at most one active row block
                 if constexpr (NA <= 1) {
                     if (cur.light) {
                         kloop(na_c, std::integral_constant<int, 0>{}, Light{});

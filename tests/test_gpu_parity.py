@@ -36,6 +36,10 @@ SMALL = {
     "tiny_fp32": ("tiny_fp32", {}),
     "multi_tile_swiglu": ("prefill_T256", dict(T=600, H=256, E=4, k=2, I=256, C=600)),
     "ragged_skew_capacity": ("skewed_bf16", dict(T=777, H=256, E=16, k=4, I=128, C=100)),
+    # experts of 280, 171, 92, 68 (heavy tiles), 52 (three-stage ring with a
+    # 64-row A part) and at most 32 rows (three-stage ring): every bf16 layout,
+    # their transitions, and the mixed tile order of light and heavy experts
+    "skewed_all_layouts": ("skewed_bf16", dict(T=400, H=512, E=16, k=2, I=256, C=400)),
     "relu2_small": ("relu2_distinct_R8", dict(H=256, I=256)),
     "decode_shared_small": ("decode_T8", dict(T=37, H=256, I=128, I_shared=256, C=37)),
     "fp8_small": ("skewed_fp8", dict(T=300, H=256, E=8, I=256, C=96)),
