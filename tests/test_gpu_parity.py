@@ -43,6 +43,9 @@ SMALL = {
     "relu2_small": ("relu2_distinct_R8", dict(H=256, I=256)),
     "decode_shared_small": ("decode_T8", dict(T=37, H=256, I=128, I_shared=256, C=37)),
     "fp8_small": ("skewed_fp8", dict(T=300, H=256, E=8, I=256, C=96)),
+    # e4m3 down projection with K = 128 (two k-tiles): the weight scales
+    # staged in LDS at a tile's start are published by its second k-tile
+    "fp8_k128": ("skewed_fp8", dict(T=300, H=256, E=8, I=128, C=96)),
     # e4m3 weights with K >= 640 in both projections (64-wide k-tiles: the
     # combine epilogue's routes staged in LDS) over two m-tiles per expert,
     # the second ragged, and a ragged last n-tile
