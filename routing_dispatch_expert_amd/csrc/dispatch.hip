@@ -146,6 +146,10 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int rank_w[kCountPerLane], ex[kCountPerLane];
     int n_bad = 0;
+    // slot of a route in its token (q mod k) with no division per step: the
+    // lane's offset mod k once, and the step base's slot advanced by 64 mod k
+    const int lmk = lane % k, s64 = kWave % k;
+    int jb = (int)(q0 % k);
     // all of this lane's ids first: one memory latency instead of one per step
 #pragma unroll
     for (int it = 0; it < kCountPerLane; ++it) {
@@ -171,12 +175,14 @@ __global__ __launch_bounds__(256) void count_rank_kernel(
         // step) are read back from memory.
         bool dup = false;
         if (inrange) {
-            const int64_t t = q / k;
-            const int j = (int)(q - t * k);
+            int j = jb + lmk;               // q mod k: the route's slot in its token
+            if (j >= k) j -= k;
             const int first = lane - j;   // lane of the token's slot 0 (may be < 0)
             dup = (peers & lt & ~((first > 0) ? (~0ull >> (64 - first)) : 0ull)) != 0;
-            for (int jj = 0; !dup && jj < -first; ++jj) dup = ids[t * k + jj] == e;
+            for (int jj = 0; !dup && jj < -first; ++jj) dup = ids[q - j + jj] == e;
         }
+        jb += s64;
+        if (jb >= k) jb -= k;
         if (inq && (!inrange || dup)) {
             e = -2;
             ++n_bad;
@@ -560,6 +566,8 @@ __global__ __launch_bounds__(kSmallThreads) void small_dispatch_kernel(
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int rank_w[kSmallSteps], ex[kSmallSteps];
     int n_bad = 0;
+    const int lmk = lane % k, s64 = kWave % k;
+    int jb = (wv * (kWave * kSmallSteps)) % k;
 #pragma unroll
     for (int it = 0; it < kSmallSteps; ++it) {
         const int q = wv * (kWave * kSmallSteps) + it * kWave + lane;
@@ -574,11 +582,14 @@ __global__ __launch_bounds__(kSmallThreads) void small_dispatch_kernel(
         }
         bool dup = false;
         if (inrange) {
-            const int t = q / k, j = q - t * k;
+            int j = jb + lmk;   // q mod k (see count_rank_kernel)
+            if (j >= k) j -= k;
             const int first = lane - j;
             dup = (peers & lt & ~((first > 0) ? (~0ull >> (64 - first)) : 0ull)) != 0;
-            for (int jj = 0; !dup && jj < -first; ++jj) dup = s_ids[t * k + jj] == e;
+            for (int jj = 0; !dup && jj < -first; ++jj) dup = s_ids[q - j + jj] == e;
         }
+        jb += s64;
+        if (jb >= k) jb -= k;
         if (inq && (!inrange || dup)) {
             e = -2;
             ++n_bad;
@@ -671,6 +682,8 @@ __global__ __launch_bounds__(kSmallThreads) void count_place_kernel(
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t pk[PER];
     int n_bad = 0;
+    const int lmk = lane % k, s64 = kWave % k;
+    int jb = q0 % k;
     // this lane's ids first: one memory latency for all of them
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
@@ -693,11 +706,14 @@ __global__ __launch_bounds__(kSmallThreads) void count_place_kernel(
         // (slots before this 64-route step are read back from memory)
         bool dup = false;
         if (inrange) {
-            const int t = q / k, j = q - t * k;
+            int j = jb + lmk;   // q mod k (see count_rank_kernel)
+            if (j >= k) j -= k;
             const int first = lane - j;
             dup = (peers & lt & ~((first > 0) ? (~0ull >> (64 - first)) : 0ull)) != 0;
-            for (int jj = 0; !dup && jj < -first; ++jj) dup = ids[t * k + jj] == e;
+            for (int jj = 0; !dup && jj < -first; ++jj) dup = ids[q - j + jj] == e;
         }
+        jb += s64;
+        if (jb >= k) jb -= k;
         if (inq && (!inrange || dup)) {
             e = -2;
             ++n_bad;
