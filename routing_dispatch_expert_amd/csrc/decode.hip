@@ -334,7 +334,7 @@ __device__ void fused_dispatch(const DecodeFused& f, int32_t* scratch, int32_t* 
             const int32_t r = hist[wv * E + e] + rank;
             row = r < f.C ? s_off[e] + r : -1;
             if (row >= 0) {
-                s_rs[row] = q;
+                s_rs[row] = q / k;   // the gate/up launch gathers: the row's token
                 if (writer) f.row_src[row] = q;
             }
         }
@@ -382,10 +382,11 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // tile table and row ranges of segment 0 when it is routed
     __shared__ int32_t s_mt[kDecodeMaxGroups + 1], s_off[kDecodeMaxGroups + 1];
-    // and, for batches of at most kDStageRows kept rows, each row's route and
-    // (down projection) its combine weight: a work item then finds its
-    // activation rows and weights in LDS instead of through two dependent
-    // global loads made while its ring is empty
+    // and, for batches of at most kDStageRows kept rows, each row's token
+    // (launches that gather their activation rows) or route and combine
+    // weight (down projection): a work item then finds its activation rows
+    // and weights in LDS instead of through two dependent global loads made
+    // while its ring is empty, and divides by k nowhere
     __shared__ int32_t s_rs[kDStageRows];
     __shared__ float s_rw[EPI0 == EPI_COMBINE ? kDStageRows : 1];
     bool staged = false;   // workgroup-uniform
@@ -406,7 +407,9 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
         if (staged) {
             for (int i = threadIdx.x; i < R; i += blockDim.x) {
                 const int32_t q = d.row_src[i];
-                s_rs[i] = q;
+                // the token of the route for launches that gather their
+                // activation rows, the route itself for the combine epilogue
+                s_rs[i] = EPI0 == EPI_COMBINE ? q : q / d.k_top;
                 if (EPI0 == EPI_COMBINE) s_rw[i] = d.route_w[q];
             }
             __syncthreads();
@@ -488,7 +491,7 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
                 if (s.offsets == nullptr) arow = (int64_t)(m0 + m);                            // uniform rows
                 else if (s.gather) {                                                             // token of the route
                     const int rr = it.base + m0 + m;
-                    arow = (int64_t)((staged && it.si == 0 ? s_rs[rr] : d.row_src[rr]) / d.k_top);
+                    arow = staged && it.si == 0 ? (int64_t)s_rs[rr] : (int64_t)(d.row_src[rr] / d.k_top);
                 }
                 else arow = (int64_t)(it.base + m0 + m);
                 it.asrc[i] = (const char*)s.A + (arow * s.lda) * 2 + c * 16;
