@@ -366,7 +366,8 @@ DecodeSeg shared_seg2(const moe_problem& p, const void* h_sh, const void* w2_sh,
 // max_rows: a bound on the rows of any group known to hold (-1: none); 8 or
 // fewer selects the 8-row activation staging.
 // fused: the launch routes and dispatches the batch itself (gate/up only).
-hipError_t run_decode(const DecodeSeg* a, const DecodeSeg* b, const int32_t* row_src, int k,
+// rs_len: entries of row_src.
+hipError_t run_decode(const DecodeSeg* a, const DecodeSeg* b, const int32_t* row_src, int64_t rs_len, int k,
                       const float* route_w, int w_dtype, int64_t route_count, int max_rows,
                       hipStream_t s, const DecodeFused* fused = nullptr) {
     DecodeArgs d = {};
@@ -381,6 +382,7 @@ hipError_t run_decode(const DecodeSeg* a, const DecodeSeg* b, const int32_t* row
         d.n_seg = 2;
     }
     d.row_src = row_src;
+    d.rs_len = row_src ? rs_len : 0;
     d.k_top = k;
     d.route_w = route_w;
     // a routed segment (tile table staged in LDS) can only be the first one
@@ -528,9 +530,9 @@ moe_status moe_expert_ffn(const moe_problem* p, const void* x_disp, const int32_
     if (decode_mode(*p)) {
         if (launch_tile_table(offsets, p->E, p->C, kDecodeBM, mt, s) != hipSuccess) return MOE_ERR_HIP;
         const DecodeSeg g1 = routed_seg1(*p, x_disp, 0, offsets, mt, w13, s13, h);
-        if (run_decode(&g1, nullptr, nullptr, p->k, nullptr, p->w_dtype, (int64_t)p->T * p->k, -1, s) != hipSuccess) return MOE_ERR_HIP;
+        if (run_decode(&g1, nullptr, nullptr, 0, p->k, nullptr, p->w_dtype, (int64_t)p->T * p->k, -1, s) != hipSuccess) return MOE_ERR_HIP;
         const DecodeSeg g2 = routed_seg2(*p, h, offsets, mt, w2, s2, EPI_STORE, y_disp);
-        return hip_status(run_decode(&g2, nullptr, nullptr, p->k, nullptr, p->w_dtype, (int64_t)p->T * p->k, -1, s));
+        return hip_status(run_decode(&g2, nullptr, nullptr, 0, p->k, nullptr, p->w_dtype, (int64_t)p->T * p->k, -1, s));
     }
     if (launch_tile_table(offsets, p->E, p->C, gemm_bm(*p), mt, s) != hipSuccess) return MOE_ERR_HIP;
     if (run_gemm1(*p, x_disp, offsets, mt, w13, s13, h, s) != hipSuccess) return MOE_ERR_HIP;
@@ -551,9 +553,9 @@ moe_status moe_shared_ffn(const moe_problem* p, const void* x, const void* w13_s
         void* h_sh = at<void>(ws, L.h_sh);
         const DecodeSeg g1 = shared_seg1(*p, x, w13_sh, h_sh);
         // shared experts: every group holds exactly T rows
-        if (run_decode(nullptr, &g1, nullptr, p->k, nullptr, MOE_BF16, (int64_t)p->T * p->k, p->T, s) != hipSuccess) return MOE_ERR_HIP;
+        if (run_decode(nullptr, &g1, nullptr, 0, p->k, nullptr, MOE_BF16, (int64_t)p->T * p->k, p->T, s) != hipSuccess) return MOE_ERR_HIP;
         const DecodeSeg g2 = shared_seg2(*p, h_sh, w2_sh, y_shared);
-        return hip_status(run_decode(nullptr, &g2, nullptr, p->k, nullptr, MOE_BF16, (int64_t)p->T * p->k, p->T, s));
+        return hip_status(run_decode(nullptr, &g2, nullptr, 0, p->k, nullptr, MOE_BF16, (int64_t)p->T * p->k, p->T, s));
     }
     return hip_status(run_shared(*p, x, w13_sh, w2_sh, at<void>(ws, L.h_sh), y_shared, s));
 }
@@ -708,13 +710,13 @@ moe_status moe_forward(const moe_problem* p, const void* x, const float* logits,
             fz.ctrl = at<int32_t>(ws, L.ctrl);
             fz.r_max = r_max_of(P);
         }
-        e = run_decode(&r1, P.n_shared ? &sh1 : nullptr, row_src, P.k, w, P.w_dtype, (int64_t)P.T * P.k, P.T, s,
+        e = run_decode(&r1, P.n_shared ? &sh1 : nullptr, row_src, r_max_of(P), P.k, w, P.w_dtype, (int64_t)P.T * P.k, P.T, s,
                        fused ? &fz : nullptr);
         if (e == hipSuccess) e = mark(m, MOE_STAGE_GEMM1, s);
         if (e != hipSuccess) return MOE_ERR_HIP;
         const DecodeSeg r2 = routed_seg2(P, h, offsets, mt, w2, s2, EPI_COMBINE, ybuf);
         const DecodeSeg sh2 = P.n_shared ? shared_seg2(P, h_sh, w2_sh, y_sh) : DecodeSeg{};
-        e = run_decode(&r2, P.n_shared ? &sh2 : nullptr, row_src, P.k, w, P.w_dtype, (int64_t)P.T * P.k, P.T, s);
+        e = run_decode(&r2, P.n_shared ? &sh2 : nullptr, row_src, r_max_of(P), P.k, w, P.w_dtype, (int64_t)P.T * P.k, P.T, s);
         if (e == hipSuccess) e = mark(m, MOE_STAGE_GEMM2, s);
         if (e == hipSuccess) e = mark(m, MOE_STAGE_SHARED, s);
         if (e == hipSuccess)

@@ -212,6 +212,7 @@ struct DecodeArgs {
     DecodeSeg seg[2];
     int n_seg;
     const int32_t* row_src;
+    int64_t rs_len;         // entries of row_src (0: none)
     int k_top;
     const float* route_w;
     int use_fused;          // segment 0's routes come from `fused`

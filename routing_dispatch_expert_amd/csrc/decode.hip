@@ -397,23 +397,51 @@ __global__ __launch_bounds__(kDWaves * 64, 1) void decode_gemm_kernel(DecodeArgs
         fused_dispatch(d.fused, (int32_t*)&rings[0][0], s_mt, s_off, s_rs, s_w4);
         staged = true;   // kept rows <= T k <= kFuseMaxQ <= kDStageRows
     } else if (d.seg[0].mt) {
-        for (int i = threadIdx.x; i <= d.seg[0].n_groups; i += blockDim.x) {
-            s_mt[i] = d.seg[0].mt[i];
-            s_off[i] = d.seg[0].offsets[i];
+        // The tables and the routes of the first rows are read in the same
+        // round trip (the kept rows, at most row_src's length, are known only
+        // from the tables): for each row, the token of its route for launches
+        // that gather their activation rows, the route itself and its weight
+        // for the combine epilogue.  Rows past the kept ones hold -1.
+        const bool want = d.seg[0].gather || EPI0 == EPI_COMBINE;
+        const int npre = want ? (int)min((int64_t)kDStageRows, d.rs_len) : 0;
+        const int ng = d.seg[0].n_groups, tid = threadIdx.x;
+        constexpr int NT = kDWaves * kWave, TJ = (kDecodeMaxGroups + NT) / NT, RJ = kDStageRows / NT;
+        static_assert(kDStageRows % NT == 0, "staged rows: whole passes of the workgroup");
+        // every load is issued before any value is used: one memory latency
+        int32_t tm[TJ], to[TJ], qv[RJ];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            const int i = tid + NT * j;
+            if (i <= ng) {
+                tm[j] = d.seg[0].mt[i];
+                to[j] = d.seg[0].offsets[i];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+            const int i = tid + NT * j;
+            if (i < npre) qv[j] = d.row_src[i];
+        }
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            const int i = tid + NT * j;
+            if (i <= ng) {
+                s_mt[i] = tm[j];
+                s_off[i] = to[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+            const int i = tid + NT * j;
+            if (i < npre) {
+                const int32_t q = qv[j];
+                s_rs[i] = EPI0 == EPI_COMBINE ? q : q / d.k_top;
+                if (EPI0 == EPI_COMBINE) s_rw[i] = q >= 0 ? d.route_w[q] : 0.0f;
+            }
         }
         __syncthreads();
         const int R = s_off[d.seg[0].n_groups];
-        staged = (d.seg[0].gather || EPI0 == EPI_COMBINE) && R <= kDStageRows;
-        if (staged) {
-            for (int i = threadIdx.x; i < R; i += blockDim.x) {
-                const int32_t q = d.row_src[i];
-                // the token of the route for launches that gather their
-                // activation rows, the route itself for the combine epilogue
-                s_rs[i] = EPI0 == EPI_COMBINE ? q : q / d.k_top;
-                if (EPI0 == EPI_COMBINE) s_rw[i] = d.route_w[q];
-            }
-            __syncthreads();
-        }
+        staged = want && R <= npre;
     }
     // work items: 32-row tiles x weight blocks; routed segments own tiles only
     // for experts with rows (tile table), uniform ones ceil(rows / 32) per group
