@@ -180,6 +180,8 @@ __device__ __forceinline__ int32_t wave_incl_scan_d(int32_t x, int lane) {
     if (lane >= 48) x += r2;
     return x;
 }
+// Exclusive scan over the workgroup's 256 threads; s_w (kDWaves ints) must
+// not be written again before the workgroup's next barrier.
 __device__ int32_t block_excl_scan_256(int32_t v, int32_t* s_w, int32_t& tot) {
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     const int32_t x = wave_incl_scan_d(v, lane);
@@ -190,7 +192,6 @@ __device__ int32_t block_excl_scan_256(int32_t v, int32_t* s_w, int32_t& tot) {
         if (w < wv) before += s_w[w];
     }
     tot = s_w[0] + s_w[1] + s_w[2] + s_w[3];
-    __syncthreads();   // s_w is reused by the next scan
     return before + x - v;
 }
 
@@ -289,8 +290,10 @@ __device__ void fused_dispatch(const DecodeFused& f, int32_t* scratch, int32_t* 
         rank = wh[e] + before;          // every lane reads before any lane writes
         if (before == 0) wh[e] += __popcll(peers);
     }
-    const int wave_bad = wave_sum_i32(n_bad);
-    if (writer && wave_bad && lane == 0) atomicAdd(&f.ctrl[CTRL_BAD_ROUTES], wave_bad);
+    if (writer) {   // workgroup-uniform: only workgroup 0 records malformed routes
+        const int wave_bad = wave_sum_i32(n_bad);
+        if (wave_bad && lane == 0) atomicAdd(&f.ctrl[CTRL_BAD_ROUTES], wave_bad);
+    }
     __syncthreads();
 
     // ---- per-expert totals and wave bases, then the scans (one expert per thread) ----
@@ -306,9 +309,13 @@ __device__ void fused_dispatch(const DecodeFused& f, int32_t* scratch, int32_t* 
         kept = run < f.C ? run : f.C;
         tiles = (kept + kDecodeBM - 1) / kDecodeBM;
     }
-    int32_t tot_k, tot_t;
-    const int32_t off_e = block_excl_scan_256(kept, s_w, tot_k);
-    const int32_t mt_e = block_excl_scan_256(tiles, s_w, tot_t);
+    // one scan of both: kept rows in the high half, 32-row tiles in the low
+    // half (sums at most T k <= 256 and E + T k / 32 <= 264: no carry between them)
+    static_assert(kFuseMaxQ < (1 << 15) && kFuseMaxE + kFuseMaxQ / kDecodeBM < (1 << 16), "packed scan halves");
+    int32_t tot_p;
+    const int32_t sc = block_excl_scan_256((kept << 16) | tiles, s_w, tot_p);
+    const int32_t off_e = sc >> 16, mt_e = sc & 0xffff;
+    const int32_t tot_k = tot_p >> 16, tot_t = tot_p & 0xffff;
     if (tid < E) {
         s_off[tid] = off_e;
         s_mt[tid] = mt_e;
