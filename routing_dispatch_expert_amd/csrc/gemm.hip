@@ -420,7 +420,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
         return t;
     };
     // Load k-tile s (in the tile's own K order) of tile t into ring slot `slot`.
-    auto issue = [&](auto lt_c, const Tile& t, int s, int slot) {
+    auto issue = [&](auto lt_c, const Tile& t, int s, int slot, int part = -1) {
         int kr = s + t.rot;
         if (kr >= nk) kr -= nk;
         const int k0 = kr * BKT;
@@ -441,13 +441,17 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
             }
             return;
         }
+        // e4m3: part 0 the B rows, part 1 + h the A half h; -1 all of them
 #pragma unroll
         for (int h = 0; h < AM; ++h)
 #pragma unroll
             for (int i = 0; i < GA; ++i)
-                if (t.la > i) dma16(Ab + t.ga[i] + (int64_t)(k0 + h * BK) * 2, la + h * A_STAGE + i * NW * 1024);
+                if ((part < 0 || part == 1 + h) && t.la > i)
+                    dma16(Ab + t.ga[i] + (int64_t)(k0 + h * BK) * 2, la + h * A_STAGE + i * NW * 1024);
+        if (part <= 0) {
 #pragma unroll
-        for (int b = 0; b < LB; ++b) dma16(Bb + t.gbase + t.gb[b] + bo * WB, lb + b * 1024);
+            for (int b = 0; b < LB; ++b) dma16(Bb + t.gbase + t.gb[b] + bo * WB, lb + b * 1024);
+        }
     };
 
     // The load ring runs across tiles: while a tile's last STG - 1
@@ -536,8 +540,15 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
                     wait_barrier_dyn(kt + 1 < nk ? lc : cn);
                 }
                 const int s = kt + SS - 1;
-                if (s < nk) issue(lt_c, cur, s, slot_of(sbase + s));
-                else if (chain) issue(lt_c, nxt, s - nk, slot_of(sbase + s));
+                // e4m3 tiles with MFMA work: the loads of k-tile kt + 2 (needed
+                // two steps from now) are spread over this step's K steps, the
+                // B rows first, so that no wave stalls in issue before its MFMAs
+                constexpr bool SPREAD = FP8 && NA > 0;
+                auto issue_part = [&](int part) {
+                    if (s < nk) issue(lt_c, cur, s, slot_of(sbase + s), part);
+                    else if (chain) issue(lt_c, nxt, s - nk, slot_of(sbase + s), part);
+                };
+                if (!SPREAD) issue_part(-1);
                 if (EPI == EPI_COMBINE && route_pf && wave < 4) {
                     // waves 0..3 stage the routes of tile rows 64 wave + lane at
                     // k-tile 1 (every wave has left the previous tile's
@@ -560,6 +571,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
                     // B row, the 8-byte piece `half` of chunk ks
                     const int lo = WIDE ? loffw[ks] : ((ks & 1) ? loff1 : loff0);   // chunk c = 2 (ks & 1) + half
                     const unsigned char* sa = slotA(lt_c, slot) + (WIDE ? 0 : (ks >> 1) * A_STAGE);
+                    if (SPREAD && ks < 1 + AM) issue_part(ks);
                     bf16x8 bv[NBW], av[NA > 0 ? NA : 1];
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb) {
@@ -587,8 +599,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
                         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
                         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                         __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-                    } else if constexpr (WIDE && NA > 0) {
-                        // all of the step's reads, then its MFMAs
+                    } else if constexpr (NA > 0) {
+                        // all of the step's reads, then its MFMAs (e4m3: the
+                        // widening of the B fragments falls in between)
                         __builtin_amdgcn_sched_group_barrier(0x100, NBW + NA, 0);
                         __builtin_amdgcn_sched_group_barrier(0x008, NBW * NA, 0);
                     }
