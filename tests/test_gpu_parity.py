@@ -401,6 +401,28 @@ def test_forward_small(key):
     assert_close(cs, out, r["out"], "out")
 
 
+# Other input seeds for cases that between them take every bf16 tile layout,
+# the e4m3 weights, the routing inside the decode gate/up launch (softmax and
+# sigmoid), capacity drops with k = 20, and more kept rows than the decode
+# kernel stages in LDS: the data-dependent paths (row spreads over m-tiles,
+# layout changes between tiles, ranks and drops) see other expert loads.
+SEEDED = ["skewed_all_layouts", "multi_tile_swiglu", "fp8_small", "decode_fused_capacity",
+          "sigmoid_decode_fused", "k20_capacity_decode", "decode_rows_over_1024"]
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("key", SEEDED)
+def test_forward_small_other_seeds(key, seed):
+    cs = dataclasses.replace(_case(key), seed=seed)
+    _say("forward small", key, "seed", seed)
+    inp_dev = synth.make_inputs(cs, DEV)
+    out, meta, n_bad = _forward_gpu(cs, inp_dev)
+    r = oracle.forward(cs, **oracle.inputs_numpy(inp_dev.to("cpu")))
+    _check_meta(cs, meta, r)
+    assert n_bad == 0
+    assert_close(cs, out, r["out"], "out")
+
+
 @pytest.mark.parametrize("T", [1, 300])   # slot-indexed decode kernels; tiled expert GEMMs
 def test_forward_e4m3_widening_exact(T):
     """Every finite e4m3 code through the expert GEMMs, bit-exact.  ReLU-square
